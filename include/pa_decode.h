@@ -1,0 +1,160 @@
+/*
+ * pa_decode.h -- C ABI of the paged-attention decode library (HIP, gfx950).
+ *
+ * The operation (one decode step).  For each sequence b < B and query head
+ * h < H, the single query vector q[b][h] attends over the context_lens[b]
+ * cached key/value rows of its sequence:
+ *
+ *   kvh      = h / (H / Hkv)                          grouped-query mapping
+ *   token t  -> blk = block_tables[b][t / block_size], slot = t % block_size
+ *   K_t      = k_cache[blk][slot][kvh][:],  V_t = v_cache[blk][slot][kvh][:]
+ *   out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) * V_t
+ *
+ * Sources: "Decoding Benchmark" docs page (MinivLLM), sections "What paged
+ * attention decode does" (shapes of q, the paged pool and the lookup pattern)
+ * and "Block table lookup mechanics" (table shape; -1 = slot never allocated);
+ * benchmark_decoding.py, the Triton (new) kernel (grouped-query mapping
+ * h // (num_heads // num_kv_heads), masking of tokens past the context and of
+ * -1 entries, fp32 accumulation, output in the query's dtype) and
+ * reference_output (the definition as gather + softmax); the
+ * flash-decoding-bench design note, implementations section (Flash-Decoding:
+ * split the context into chunks processed in parallel, each keeping local
+ * max / sum / weighted values, merged by a reduction afterwards).
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   q, out          [B][H][d]                       dtype
+ *   k_cache,v_cache [num_pool_blocks][block_size][Hkv][d]   dtype
+ *   block_tables    [B][max_blocks]                 int32
+ *   context_lens    [B]                             int32
+ * dtype (PA_DTYPE_*) applies to q, k_cache, v_cache and out alike.  Scores,
+ * softmax statistics and accumulation are fp32; bf16 outputs are rounded to
+ * nearest even.
+ *
+ * Conventions:
+ *   - Supported shapes: d = 128, block_size = 16, H % Hkv == 0 with
+ *     H / Hkv in {1, 2, 4, 8, 16}.  Others return PA_ERR_UNSUPPORTED.
+ *   - All calls only enqueue work on `stream` (a hipStream_t, NULL = the null
+ *     stream); nothing synchronises with the host.  The return code reports
+ *     errors the host can see: argument validation (checked before any HIP
+ *     call) and launch failures.  Faults inside a kernel surface later, from
+ *     the HIP runtime, and leave the HIP context unusable.
+ *   - q, k_cache, v_cache, out and workspace must be 16-byte aligned;
+ *     block_tables and context_lens 4-byte aligned.  out must not overlap q,
+ *     k_cache or v_cache.
+ *   - The caller owns every buffer.  The library keeps no pointer past the
+ *     call, except the workspace it allocates itself (see pa_decode).
+ *   - B == 0 is a no-op that returns PA_OK.
+ *   - Device-side preconditions the host cannot check without a copy:
+ *     context_lens[b] is clamped to [0, max_blocks * block_size]; a negative
+ *     table entry inside the context (-1) removes that block's tokens from
+ *     the softmax; every other entry used must be a valid pool block.  A
+ *     sequence with no live token gets an all-zero output row.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+
+enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    PA_ERR_SHAPE = -2,       /* negative or inconsistent sizes (e.g. H % Hkv != 0) */
+    PA_ERR_UNSUPPORTED = -3, /* valid but not built: d, block_size or H/Hkv       */
+    PA_ERR_DTYPE = -4,       /* dtype is not a pa_dtype_t value                   */
+    PA_ERR_ALIGN = -5,       /* a pointer breaks the alignment rule               */
+    PA_ERR_WORKSPACE = -6,   /* caller workspace missing or too small             */
+    PA_ERR_HIP = -7,         /* a HIP runtime call or a launch failed             */
+    PA_ERR_DEVICE = -8,      /* no current HIP device                             */
+    PA_ERR_ALIAS = -9,       /* out overlaps an input                             */
+    PA_ERR_VALUE = -10       /* scale not finite, or a negative count             */
+};
+
+/*
+ * One decode step (the signature the docs page's kernel launch wraps:
+ * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
+ * shape parameters).  Picks the number of context partitions with
+ * pa_choose_partitions for the current device: one partition runs a single
+ * kernel that writes out directly; more run the split kernel, which writes
+ * partial (max, sum, weighted values) per partition into a workspace, then
+ * the merge kernel.  The workspace is allocated by the library on first need
+ * per (device, stream) and grown when a larger one is needed (growing
+ * synchronises `stream` once); pa_release frees it.
+ * max_blocks is the width of block_tables (its row stride).
+ * Returns PA_OK or a negative PA_ERR_* code.
+ */
+int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, int B, int H, int Hkv,
+              int d, int block_size, int max_blocks, float scale, int dtype, void *stream);
+
+/*
+ * pa_decode with the choices exposed.
+ *   num_partitions   0 = heuristic (as pa_decode), 1 = single pass, n > 1 =
+ *                    split into n partitions (reduced to ceil(max_blocks /
+ *                    ceil(max_blocks / n)) so none is empty by construction).
+ *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
+ *                    treated like -1 instead of being read (a guard against
+ *                    out-of-range ids).
+ *   workspace        NULL = library-owned (as pa_decode); else a device buffer
+ *                    of workspace_bytes >= pa_workspace_bytes(B, H, d, P) for
+ *                    the partition count P actually used, else
+ *                    PA_ERR_WORKSPACE.  Unused when P == 1.
+ */
+int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, int B, int H, int Hkv,
+                 int d, int block_size, int max_blocks, float scale, int dtype, void *stream,
+                 int num_partitions, long long num_pool_blocks, void *workspace,
+                 size_t workspace_bytes);
+
+/*
+ * The two halves of the split path, for callers that schedule them apart or
+ * time them separately (Flash-Decoding's per-chunk pass and its merge).
+ * pa_decode_partials runs only the split kernel: for every (b, h) and
+ * partition p < P it writes the partition's running max (log2 units, i.e.
+ * of scale * log2(e) * q.K), its normaliser and its unnormalised weighted sum
+ * of V rows into `workspace` (layout: [B][H][P] float pairs (max, sum),
+ * padded to 256 bytes, then [B][H][P][d] float).  An empty partition stores
+ * (-1e30, 0, zeros).  pa_merge_partials combines them into out.  num_partitions
+ * must be >= 1 and is used as given (P = num_partitions).
+ */
+int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, int B, int H,
+                       int Hkv, int d, int block_size, int max_blocks, float scale, int dtype,
+                       int num_partitions, long long num_pool_blocks, void *workspace,
+                       size_t workspace_bytes, void *stream);
+int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, int B, int H,
+                      int d, int num_partitions, int dtype, void *stream);
+
+/* Workspace bytes the split path needs for P partitions (0 when P <= 1). */
+size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
+
+/*
+ * The launch heuristic (pure; no HIP call).  Work units are the B * Hkv
+ * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
+ * they already cover the device (>= num_cus) it returns 1.  Otherwise it
+ * splits each unit's context into enough partitions to give about num_cus
+ * workgroups, keeping at least 8 blocks of block_size tokens per partition,
+ * then evens the partitions out.  Returns >= 1 (1 for non-positive inputs).
+ */
+int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
+
+/* Compute units of HIP device `device` (cached), or a negative PA_ERR_*. */
+int pa_device_num_cus(int device);
+
+/* Static text for a return code. */
+const char *pa_strerror(int code);
+
+/* Frees every library-owned workspace (synchronises the devices that own one). */
+void pa_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

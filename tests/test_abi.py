@@ -1,0 +1,163 @@
+"""The C-ABI library on the CPU: it loads, exports what include/pa_decode.h
+declares, and rejects invalid arguments before any HIP call.  No compute call
+is made here (there is no GPU); the fake device addresses below are never
+dereferenced because validation fails first."""
+import math
+import os
+import re
+
+import pytest
+
+import paged_attention_decode_pa_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pa_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pa.load()
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(pa.EXPORTS)
+
+
+def test_strerror_covers_codes():
+    for code in range(0, -11, -1):
+        s = pa.strerror(code)
+        assert s and s != "unknown error code", code
+    assert pa.strerror(-99) == "unknown error code"
+
+
+@pytest.mark.parametrize("B,Hkv,max_blocks,cus,expect", [
+    (2, 8, 4, 256, 1),        # 60 tokens: too short to split (needs 8 blocks/partition)
+    (1, 8, 32, 256, 4),       # 512 tokens: capped at 32 / 8 partitions
+    (16, 8, 16, 256, 2),      # 128 units -> 2 partitions of 8 blocks
+    (4, 8, 128, 256, 8),      # 32 units -> 8 partitions of 16 blocks
+    (1, 8, 1024, 256, 32),    # 8 units -> 32 partitions of 32 blocks
+    (32, 8, 1024, 256, 1),    # 256 units already fill 256 CUs
+    (1, 1, 100, 256, 12),     # capped at 100 // 8 = 12, evened to 12 (9 blocks each)
+    (1, 8, 7, 256, 1),
+    (0, 8, 10, 256, 1),
+    (3, 8, 1000, 0, 1),
+])
+def test_choose_partitions(B, Hkv, max_blocks, cus, expect):
+    assert pa.pa_choose_partitions(B, Hkv, max_blocks, 16, cus) == expect
+
+
+def test_choose_partitions_properties():
+    for B in (1, 2, 3, 5, 8, 31):
+        for Hkv in (1, 2, 8):
+            for mb in (1, 7, 8, 9, 64, 129, 1000, 4097):
+                for cus in (80, 256, 304):
+                    P = pa.pa_choose_partitions(B, Hkv, mb, 16, cus)
+                    assert 1 <= P <= max(1, mb)
+                    bpp = math.ceil(mb / P)
+                    # no empty partition by construction
+                    assert (P - 1) * bpp < mb
+                    if P > 1:
+                        assert bpp >= 8
+                        assert B * Hkv < cus
+
+
+def test_workspace_bytes():
+    assert pa.pa_workspace_bytes(1, 32, 128, 1) == 0
+    assert pa.pa_workspace_bytes(0, 32, 128, 4) == 0
+    # (max, sum) pairs padded to 256 bytes, then the fp32 partial sums
+    assert pa.pa_workspace_bytes(1, 32, 128, 32) == 8192 + 32 * 32 * 128 * 4
+    assert pa.pa_workspace_bytes(4, 32, 128, 3) == 3072 + 4 * 32 * 3 * 128 * 4
+    assert pa.pa_workspace_bytes(1, 3, 128, 3) == 256 + 3 * 3 * 128 * 4
+    assert pa.pa_workspace_bytes(1, 1, 128, 2) == 256 + 2 * 128 * 4
+
+
+FAKE = dict(out=0x100000, q=0x200000, k=0x300000, v=0x400000, t=0x500000, n=0x600000)
+
+
+def call(**kw):
+    a = dict(FAKE, B=2, H=32, Hkv=8, d=128, bs=16, mb=4, scale=0.088, dtype=1)
+    a.update(kw)
+    return pa.load().pa_decode(a["out"], a["q"], a["k"], a["v"], a["t"], a["n"], a["B"], a["H"],
+                               a["Hkv"], a["d"], a["bs"], a["mb"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(H=24, Hkv=8), pa.PA_ERR_UNSUPPORTED),   # G = 3
+    (dict(H=32, Hkv=6), pa.PA_ERR_SHAPE),         # H % Hkv != 0
+    (dict(B=-1), pa.PA_ERR_SHAPE),
+    (dict(H=0), pa.PA_ERR_SHAPE),
+    (dict(mb=0), pa.PA_ERR_SHAPE),
+    (dict(dtype=2), pa.PA_ERR_DTYPE),
+    (dict(dtype=-1), pa.PA_ERR_DTYPE),
+    (dict(scale=float("nan")), pa.PA_ERR_VALUE),
+    (dict(scale=float("inf")), pa.PA_ERR_VALUE),
+    (dict(q=0), pa.PA_ERR_NULL),
+    (dict(out=0), pa.PA_ERR_NULL),
+    (dict(t=0), pa.PA_ERR_NULL),
+    (dict(k=0x300008), pa.PA_ERR_ALIGN),
+    (dict(out=0x100004), pa.PA_ERR_ALIGN),
+    (dict(n=0x600002), pa.PA_ERR_ALIGN),
+    (dict(out=0x200000 + 4096), pa.PA_ERR_ALIAS),   # inside q's 2*32*128*2 bytes
+    (dict(out=0x300000), pa.PA_ERR_ALIAS),
+])
+def test_validation_codes(kw, code):
+    assert call(**kw) == code
+
+
+def test_empty_batch_is_a_noop():
+    assert call(B=0) == pa.PA_OK
+    assert call(B=0, q=0, out=0) == pa.PA_OK
+
+
+def test_valid_call_without_device_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the launch path is covered by the GPU tests")
+    assert call() == pa.PA_ERR_DEVICE
+
+
+def test_ex_and_split_half_validation():
+    lib = pa.load()
+    args = [FAKE["out"], FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128,
+            16, 64, 0.088, 1, None]
+    assert lib.pa_decode_ex(*args, -1, 0, None, 0) == pa.PA_ERR_VALUE
+    assert lib.pa_decode_ex(*args, 0, -5, None, 0) == pa.PA_ERR_VALUE
+    assert lib.pa_decode_ex(*args, 4, 0, 0x700004, 1 << 20) == pa.PA_ERR_ALIGN
+    part = [FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128, 16, 64, 0.088,
+            1]
+    assert lib.pa_decode_partials(*part, 0, 0, 0x700000, 1 << 20, None) == pa.PA_ERR_VALUE
+    assert lib.pa_decode_partials(*part, 4, 0, None, 1 << 20, None) == pa.PA_ERR_WORKSPACE
+    need = pa.pa_workspace_bytes(1, 32, 128, 4)
+    assert lib.pa_decode_partials(*part, 4, 0, 0x700000, need - 1, None) == pa.PA_ERR_WORKSPACE
+    assert lib.pa_decode_partials(*part, 5000, 0, 0x700000, 1 << 30, None) == \
+        pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_merge_partials(FAKE["out"], None, need, 1, 32, 128, 4, 1, None) == \
+        pa.PA_ERR_WORKSPACE
+    assert lib.pa_merge_partials(FAKE["out"], 0x700000, need - 1, 1, 32, 128, 4, 1, None) == \
+        pa.PA_ERR_WORKSPACE
+    assert lib.pa_merge_partials(FAKE["out"], 0x700000, need, 1, 32, 64, 4, 1, None) == \
+        pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_merge_partials(0x700000 + 64, 0x700000, need, 1, 32, 128, 4, 1, None) == \
+        pa.PA_ERR_ALIAS
+    assert lib.pa_merge_partials(FAKE["out"], 0x700000, need, 0, 32, 128, 4, 1, None) == pa.PA_OK
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(2, 32, 128, dtype=torch.float16)
+    k = torch.zeros(4, 16, 8, 128, dtype=torch.float16)
+    t = torch.zeros(2, 2, dtype=torch.int32)
+    n = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(pa.PaError):
+        pa.decode(q, k, k, t, n, 0.1)
+    with pytest.raises(pa.PaError):
+        pa.decode(q.float(), k.float(), k.float(), t.long(), n, 0.1)

@@ -1,0 +1,235 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI, on the GPU.
+
+Covers the five named workloads at full size (heuristic partition count, the
+configuration the benchmark times), forced partition counts, ragged and
+empty contexts, -1 holes, every supported group size, both dtypes, and the
+invariants that must hold bitwise on the GPU too (block permutation, NaN in
+unused slots, context length 1, repeatability, split halves == fused call).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pa_inputs as pi
+import paged_attention_decode_pa_amd as pa
+
+from gpu_util import (DeviceCase, assert_close, check_host_preconditions, run_gpu, say,
+                      to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seed_base", [0, 1000])
+def test_workload_parity_heuristic(gpu, cid, seed_base):
+    case = pi.make_config_case(cid, seed=seed_base + cid)
+    say(f"workload {cid} seed {seed_base + cid}: pa_decode (heuristic)")
+    out = run_gpu(case, gpu)
+    ref = oracle.decode_case(case)
+    assert_close(to_f64(out), ref, case.dtype, f"workload {cid}")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("parts", [1, 2, 3, 7, 64, 10 ** 6])
+def test_workload_parity_forced_partitions(gpu, cid, parts):
+    case = pi.make_config_case(cid)
+    say(f"workload {cid}: pa_decode_ex num_partitions={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    ref = oracle.decode_case(case)
+    assert_close(to_f64(out), ref, case.dtype, f"workload {cid} P={parts}")
+
+
+RAGGED = [
+    # B, lens, H, Hkv, holes
+    (7, [0, 1, 15, 16, 17, 100, 257], 32, 8, []),
+    (3, [64, 300, 33], 16, 16, [(1, 2), (1, 3)]),
+    (4, [129, 5, 48, 200], 8, 4, [(0, 0)]),
+    (2, [500, 31], 64, 8, [(0, 10)]),
+    (3, [90, 90, 1], 32, 2, []),
+    (2, [1000, 77], 16, 1, [(0, 0), (0, 62)]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", RAGGED)
+@pytest.mark.parametrize("parts", [0, 1, 3, 16])
+def test_ragged_lengths_holes_and_groups(gpu, dtype, shape, parts):
+    B, lens, H, Hkv, holes = shape
+    max_blocks = max(math.ceil(n / 16) for n in lens) + 1
+    need = sum(math.ceil(n / 16) for n in lens)
+    case = pi.make_case(B, lens, H, Hkv, 128, 16, dtype=dtype, seed=sum(lens) + H,
+                        max_blocks=max_blocks, pool=need + 5, holes=holes)
+    say(f"ragged {lens} H={H} Hkv={Hkv} {dtype} P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    ref = oracle.decode_case(case)
+    assert_close(to_f64(out), ref, dtype, f"ragged {lens} G={H // Hkv} P={parts}")
+    for b, n in enumerate(lens):
+        live = [t for t in range(n) if case.block_tables[b, t // 16] >= 0]
+        if not live:
+            assert (out[b].float() == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_permutation_is_bitwise_invariant(gpu, dtype):
+    case = pi.make_case(3, [200, 47, 16], 32, 8, 128, 16, dtype=dtype, seed=5, pool=20)
+    perm = np.random.default_rng(3).permutation(20).astype(np.int32)
+    moved = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(20)
+    for name in ("k_cache", "v_cache", "k_bits", "v_bits"):
+        arr = getattr(case, name)
+        if arr is not None:
+            setattr(moved, name, np.ascontiguousarray(arr[inv]))
+    t = case.block_tables.copy()
+    t[t >= 0] = perm[t[t >= 0]]
+    moved.block_tables = t
+    for parts in (0, 1, 4):
+        say(f"permutation {dtype} P={parts}")
+        a = run_gpu(case, gpu, num_partitions=parts)
+        b = run_gpu(moved, gpu, num_partitions=parts)
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_context_len_one_returns_v_row_bitwise(gpu, dtype):
+    case = pi.make_case(4, [1, 1, 1, 1], 32, 8, 128, 16, dtype=dtype, seed=6, max_blocks=40,
+                        pool=12)
+    for parts in (0, 1, 5):
+        say(f"ctx=1 {dtype} P={parts}")
+        out = run_gpu(case, gpu, num_partitions=parts).cpu()
+        for b in range(4):
+            blk = case.block_tables[b, 0]
+            for h in range(32):
+                if dtype == "bf16":
+                    row = torch.from_numpy(case.v_bits[blk, 0, h // 4].view(np.int16))
+                    assert torch.equal(out[b, h].view(torch.int16), row)
+                else:
+                    assert torch.equal(out[b, h], torch.from_numpy(case.v_cache[blk, 0, h // 4]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_in_unused_slots_never_leaks(gpu, dtype):
+    case = pi.make_case(4, [37, 16, 3, 250], 32, 8, 128, 16, dtype=dtype, seed=7,
+                        max_blocks=20, pool=30)
+    poisoned = pi.poison_unused(case)
+    clean = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    clean.block_tables = poisoned.block_tables
+    for parts in (0, 1, 3):
+        say(f"nan poison {dtype} P={parts}")
+        a = run_gpu(clean, gpu, num_partitions=parts)
+        b = run_gpu(poisoned, gpu, num_partitions=parts)
+        assert torch.equal(a, b)
+        assert_close(to_f64(b), oracle.decode_case(clean), dtype, "poisoned")
+
+
+def test_identical_keys_give_mean_of_v(gpu):
+    case = pi.make_case(2, [300, 45], 32, 8, 128, 16, dtype="bf16", seed=8, pool=30)
+    case.k_bits[:] = case.k_bits[0, 0, 0]
+    case.k_cache = pi.bf16_bits_to_f32(case.k_bits)
+    say("identical keys")
+    out = to_f64(run_gpu(case, gpu))
+    for b, n in enumerate([300, 45]):
+        for kvh in range(8):
+            rows = np.array([case.v_cache[case.block_tables[b, t // 16], t % 16, kvh]
+                             for t in range(n)], dtype=np.float64)
+            mean = rows.mean(axis=0)
+            for h in range(kvh * 4, kvh * 4 + 4):
+                assert np.abs(out[b, h] - mean).max() <= 2e-3 + 1e-2 * np.abs(mean).max()
+
+
+def test_gqa_mapping_constant_v(gpu):
+    case = pi.make_case(2, [70, 300], 32, 8, 128, 16, dtype="f32", seed=9, pool=30)
+    for kvh in range(8):
+        case.v_cache[:, :, kvh, :] = kvh
+    say("gqa constant V")
+    out = to_f64(run_gpu(case, gpu))
+    for h in range(32):
+        assert np.abs(out[:, h] - h // 4).max() <= 1e-5
+
+
+def test_repeatable_bitwise(gpu):
+    case = pi.make_config_case(5)
+    say("repeatability workload 5")
+    a = run_gpu(case, gpu)
+    b = run_gpu(case, gpu)
+    assert torch.equal(a, b)
+
+
+def test_split_halves_equal_fused_call(gpu):
+    case = pi.make_config_case(4)
+    d = DeviceCase(case, gpu)
+    P = 8
+    nbytes = pa.pa_workspace_bytes(case.batch, 32, 128, P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    out_a = torch.empty_like(d.q)
+    out_b = torch.empty_like(d.q)
+    say("split halves vs fused, caller workspace")
+    pa.pa_decode_partials(*d.args(), P, 0, ws, nbytes)
+    pa.pa_merge_partials(out_a, ws, nbytes, case.batch, 32, 128, P, d.dtype)
+    pa.pa_decode_ex(out_b, *d.args(), None, P, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    out_c = run_gpu(case, gpu, num_partitions=P)  # library-owned workspace
+    assert torch.equal(out_a, out_c)
+    # partial statistics: every partition of every (b, h) is non-empty here
+    ml = ws[: case.batch * 32 * P * 8].view(torch.float32).view(case.batch, 32, P, 2).cpu()
+    assert (ml[..., 1] > 0).all() and torch.isfinite(ml).all()
+
+
+def test_pool_guard_skips_out_of_range_ids(gpu):
+    # entries >= num_pool_blocks are treated like -1; the device pool has two
+    # extra blocks so that those ids would still be in bounds without the guard
+    case = pi.make_case(2, [160, 90], 32, 8, 128, 16, dtype="bf16", seed=10, pool=20)
+    pool = case.num_pool_blocks
+    guarded = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    t = case.block_tables.copy()
+    t[0, 3] = pool
+    t[1, 5] = pool + 1
+    guarded.block_tables = t
+    expect_case = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    te = case.block_tables.copy()
+    te[0, 3] = -1
+    te[1, 5] = -1
+    expect_case.block_tables = te
+    d = DeviceCase(guarded, gpu, extra_pool_blocks=2)
+    out = torch.empty_like(d.q)
+    say("pool guard")
+    pa.pa_decode_ex(out, *d.args(), None, 0, pool, None, 0)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(expect_case), "bf16", "pool guard")
+
+
+def test_non_default_stream(gpu):
+    case = pi.make_config_case(3)
+    s = torch.cuda.Stream()
+    say("side stream")
+    with torch.cuda.stream(s):
+        d = DeviceCase(case, gpu)
+        out = torch.empty_like(d.q)
+        pa.pa_decode(out, *d.args(), s)
+    s.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", "side stream")
+
+
+def test_empty_batch_launches_nothing(gpu):
+    q = torch.empty(0, 32, 128, dtype=torch.bfloat16, device=gpu)
+    k = torch.empty(4, 16, 8, 128, dtype=torch.bfloat16, device=gpu)
+    t = torch.empty(0, 4, dtype=torch.int32, device=gpu)
+    n = torch.empty(0, dtype=torch.int32, device=gpu)
+    out = pa.decode(q, k, k, t, n, 0.1)
+    assert out.shape == (0, 32, 128)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("parts", [0, 1, 4096])
+def test_long_context_many_chunks(gpu, dtype, parts):
+    # 131072 tokens = 8192 blocks: a single pass walks 2048 blocks per wave
+    # (32 table chunks of 64); 4096 partitions is the largest count
+    case = pi.make_case(1, 131072 - 9, 32, 8, 128, 16, dtype=dtype, seed=11, pool=8192)
+    say(f"long context {dtype} P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    ref = oracle.decode_case(case)
+    assert_close(to_f64(out), ref, dtype, f"long P={parts}")
