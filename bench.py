@@ -1,0 +1,323 @@
+"""Benchmark of the paged-attention decode step on one MI355X.
+
+A step is one pa_decode call: the whole decode (split kernel + merge kernel,
+or the single-pass kernel) over one batch of synthetic, seeded inputs.  The
+headline workload is the largest one, bf16 B=1, context 16384, 32 query / 8 kv
+heads, head_dim 128, block_size 16, with the partition count chosen by the
+library's heuristic.
+
+Timing: inputs are resident in HBM before the timed region.  Each step uses
+the next of N distinct copies of (K/V pool, q, table, lengths, out), N chosen
+so the copies span >= 1 GiB, so the 256 MB Infinity Cache cannot serve a
+step's K/V reads from the previous visit.  W warm-up steps, then exactly K
+steps between two synchronisations, recorded by HIP events on the stream the
+kernels run on.  By default the K steps are replayed from one HIP graph
+(capture of the same K pa_decode calls) so host launch overhead does not set
+the pace; --eager times plain launches.
+
+Output: one JSON line (rank 0, N = 1).  value = algorithmic bytes per step /
+step time (GB/s); algorithmic bytes = every live K and V row once per kv head
++ q + out + block table.  A step of the headline workload is one launch of
+the split kernel with its fused merge, so "roofline" (the dominant kernel)
+uses the same timed region: algorithmic bytes per launch / average launch
+time.  "cpu_baseline" times the fp64 C oracle on the host's cores on the same
+workload.  "per_config" adds the other workloads and the single-pass runs.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode step μs and achieved HBM GB/s (% of MI355X peak) per config"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+ROTATION_BYTES = 1 << 30       # distinct bytes the copies must span
+MAX_COPIES = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--eager", action="store_true", help="time plain launches, no HIP graph")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain elementwise copy of this many MiB (counter scale)")
+    return ap.parse_args()
+
+
+class Workload:
+    """N rotation copies of one workload's inputs on the device."""
+
+    def __init__(self, cid, dev, num_partitions=0, seed=None):
+        import torch
+        import pa_inputs as pi
+        import paged_attention_decode_pa_amd as pa
+
+        self.cid = cid
+        self.case = pi.make_config_case(cid, seed)
+        c = self.case
+        self.bytes = c.algorithmic_bytes()
+        self.ncopies = max(2, min(MAX_COPIES, math.ceil(ROTATION_BYTES / self.bytes)))
+        if c.dtype == "bf16":
+            conv = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+            q0, k0, v0 = conv(c.q_bits), conv(c.k_bits), conv(c.v_bits)
+        else:
+            q0, k0, v0 = (torch.from_numpy(x).to(dev) for x in (c.q, c.k_cache, c.v_cache))
+        t0 = torch.from_numpy(c.block_tables).to(dev)
+        n0 = torch.from_numpy(c.context_lens).to(dev)
+        self.copies = []
+        for i in range(self.ncopies):
+            if i == 0:
+                q, k, v, t, n = q0, k0, v0, t0, n0
+            else:
+                q, k, v, t, n = (x.clone() for x in (q0, k0, v0, t0, n0))
+            self.copies.append(dict(q=q, k=k, v=v, t=t, n=n, out=torch.empty_like(q0)))
+        self.dtype = pa.dtype_code(q0.dtype)
+        self.cus = pa.pa_device_num_cus(dev.index or 0)
+        self.P = (pa.pa_choose_partitions(c.batch, c.num_kv_heads, c.max_blocks, c.block_size,
+                                          self.cus) if num_partitions == 0
+                  else min(num_partitions, c.max_blocks))
+        if self.P > 1:
+            bpp = math.ceil(c.max_blocks / self.P)
+            self.P = math.ceil(c.max_blocks / bpp)
+        self.num_partitions = num_partitions
+        self.lib = pa.load()
+
+    def step(self, i, stream):
+        """One whole decode step on copy i % N (pa_decode / pa_decode_ex)."""
+        c, x = self.case, self.copies[i % self.ncopies]
+        if self.num_partitions == 0:
+            rc = self.lib.pa_decode(x["out"].data_ptr(), x["q"].data_ptr(), x["k"].data_ptr(),
+                                    x["v"].data_ptr(), x["t"].data_ptr(), x["n"].data_ptr(),
+                                    c.batch, c.num_heads, c.num_kv_heads, c.head_dim,
+                                    c.block_size, c.max_blocks, float(c.scale), self.dtype,
+                                    stream)
+        else:
+            rc = self.lib.pa_decode_ex(x["out"].data_ptr(), x["q"].data_ptr(), x["k"].data_ptr(),
+                                       x["v"].data_ptr(), x["t"].data_ptr(), x["n"].data_ptr(),
+                                       c.batch, c.num_heads, c.num_kv_heads, c.head_dim,
+                                       c.block_size, c.max_blocks, float(c.scale), self.dtype,
+                                       stream, self.num_partitions, 0, None, 0)
+        if rc != 0:
+            raise RuntimeError(f"pa_decode failed: {rc}")
+
+    def single_launch(self):
+        """True when one step is one kernel launch: the single pass, or the
+        fused split (heuristic partitions, library-owned workspace)."""
+        return self.P == 1 or self.num_partitions == 0
+
+    def kernel_name(self):
+        if self.P == 1:
+            return "pa_decode_kernel (single pass)"
+        if self.num_partitions == 0:
+            return "pa_decode_kernel (split, fused merge)"
+        return "pa_decode_kernel (split) + pa_merge_kernel"
+
+
+def time_region(fn, steps, warmup, use_graph):
+    """Seconds per call of fn(i, stream) over exactly `steps` calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    if use_graph:
+        # warm up on the capture stream itself: the library keeps its split
+        # workspace per stream and must not allocate while capturing
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for i in range(warmup):
+                fn(i, cap.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            g.capture_begin()
+            for i in range(steps):
+                fn(i, cap.cuda_stream)
+            g.capture_end()
+        torch.cuda.synchronize()
+        g.replay()          # one untimed replay
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        del g
+    else:
+        for i in range(warmup):
+            fn(i, sh)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            fn(i, sh)
+        end.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / steps
+
+
+def parity_gate(w):
+    """Copy 0 against the oracle at the stated tolerance, every copy bitwise equal."""
+    import torch
+    import oracle
+    torch.cuda.synchronize()
+    ref = oracle.decode_case(w.case)
+    got = w.copies[0]["out"].float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    if w.case.dtype == "f32":
+        ok = err.max() <= 1e-5
+    else:
+        ok = bool((err <= 2e-3 + 1e-2 * np.abs(ref)).all())
+    same = all(torch.equal(x["out"], w.copies[0]["out"]) for x in w.copies)
+    return ok and same, float(err.max())
+
+
+def measure(cid, dev, steps, warmup, use_graph, num_partitions=0):
+    w = Workload(cid, dev, num_partitions)
+    for i in range(w.ncopies):
+        w.step(i, None)
+    ok, max_err = parity_gate(w)
+    if not ok:
+        raise SystemExit(f"workload {cid}: parity gate FAILED (max err {max_err:.3e}); "
+                         "timing would be meaningless")
+    t_step = time_region(w.step, steps, warmup, use_graph)
+    return w, t_step, max_err
+
+
+def cpu_baseline(cid, budget_s):
+    import oracle
+    import pa_inputs as pi
+    case = pi.make_config_case(cid)
+    threads = oracle.max_threads()
+    oracle.decode_case(case, threads=threads)  # load, first touch
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_case(case, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (reps >= 1 and el * (reps + 1) / reps > 3 * budget_s):
+            break
+    per = el / reps
+    return dict(value=round(case.algorithmic_bytes() / per / 1e9, 4), unit="GB/s",
+                cores=threads, kind="oracle",
+                sample=f"the full workload-{cid} step ({case.name}), {reps} repetitions, "
+                       f"{per * 1e3:.1f} ms each, fp64 C oracle with OpenMP over (b, h)",
+                ms_per_step=round(per * 1e3, 3))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step has no multi-GPU path in this library)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_attention_decode_pa_amd as pa
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    pa.load()
+    dev = torch.device("cuda:0")
+    use_graph = not args.eager
+
+    per_config = []
+    if not args.no_per_config:
+        plan = [(c, 0) for c in (1, 2, 3, 4, 5) if c != args.workload] + [(4, 1), (5, 1)]
+        for cid, parts in plan:
+            w, ts, err = measure(cid, dev, min(args.steps, 1000), args.warmup, use_graph, parts)
+            per_config.append(dict(
+                workload=cid, name=w.case.name, partitions=w.P,
+                path="single-pass" if w.P == 1 else "split-KV + merge",
+                us_per_step=round(ts * 1e6, 3), GBps=round(w.bytes / ts / 1e9, 1),
+                pct_of_peak=round(100 * w.bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
+                launches_per_step=1 if w.single_launch() else 2, max_abs_err=err,
+                rotation_copies=w.ncopies, algorithmic_bytes=w.bytes))
+            log(f"workload {cid} P={w.P}: {ts * 1e6:.2f} us/step "
+                f"{w.bytes / ts / 1e9:.0f} GB/s")
+            del w
+            torch.cuda.empty_cache()
+
+    w, t_step, err = measure(args.workload, dev, args.steps, args.warmup, use_graph)
+    gbs = w.bytes / t_step / 1e9
+    log(f"headline workload {args.workload} P={w.P}: {t_step * 1e6:.2f} us/step {gbs:.0f} GB/s")
+    if not w.single_launch():
+        raise SystemExit("the headline step must be a single kernel launch")
+    # the step is one launch of the dominant kernel: its timed region is the step's
+    t_dom, dom_bytes = t_step, w.bytes
+    dom_gbs = dom_bytes / t_dom / 1e9
+    c = w.case
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.randn(n // 2, device=dev).to(torch.bfloat16)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read and {n} bytes written per launch, 5 launches")
+
+    base = None
+    if args.cpu_seconds > 0:
+        base = cpu_baseline(args.workload, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 6),
+        "us_per_step": round(t_step * 1e6, 3),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": c.name + (" split-KV (Flash-Decoding) + merge" if w.P > 1
+                                  else " single-pass"),
+            "batch": c.batch, "context_len": int(c.context_lens[0]),
+            "num_heads": c.num_heads, "num_kv_heads": c.num_kv_heads,
+            "head_dim": c.head_dim, "block_size": c.block_size,
+            "pool_blocks": c.num_pool_blocks, "num_partitions": w.P,
+            "algorithmic_bytes_per_step": w.bytes, "rotation_copies": w.ncopies,
+            "timing": "HIP graph replay of K steps" if use_graph else "eager launches",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": w.kernel_name(),
+            "achieved": round(dom_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(t_dom * 1e6, 3),
+            "launches_per_step": 1,
+            "bytes_per_launch": dom_bytes,
+        },
+        "cpu_baseline": base,
+        "max_abs_err": err,
+        "per_config": per_config,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

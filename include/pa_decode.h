@@ -79,13 +79,17 @@ enum {
 /*
  * One decode step (the signature the docs page's kernel launch wraps:
  * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
- * shape parameters).  Picks the number of context partitions with
- * pa_choose_partitions for the current device: one partition runs a single
- * kernel that writes out directly; more run the split kernel, which writes
- * partial (max, sum, weighted values) per partition into a workspace, then
- * the merge kernel.  The workspace is allocated by the library on first need
- * per (device, stream) and grown when a larger one is needed (growing
- * synchronises `stream` once); pa_release frees it.
+ * shape parameters).  Picks the number of context partitions P with
+ * pa_choose_partitions for the current device.  P == 1 runs one kernel that
+ * writes out directly.  P > 1 runs the split kernel in its fused form: every
+ * workgroup writes its partition's (max, sum, weighted values) to a
+ * library-owned workspace and takes an atomic ticket; the last workgroup of
+ * each (sequence, kv head) merges the P partials and writes out.  The partials
+ * buffer and the ticket buffer (zeroed when allocated; every call leaves its
+ * tickets zero) are allocated on first need per (device, stream) and grown
+ * when larger ones are needed (growing synchronises `stream` once).  Calls on
+ * one stream are ordered by the stream; do not capture the first call on a
+ * stream into a graph (it allocates).  pa_release frees them.
  * max_blocks is the width of block_tables (its row stride).
  * Returns PA_OK or a negative PA_ERR_* code.
  */
@@ -101,10 +105,13 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
  *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
  *                    treated like -1 instead of being read (a guard against
  *                    out-of-range ids).
- *   workspace        NULL = library-owned (as pa_decode); else a device buffer
- *                    of workspace_bytes >= pa_workspace_bytes(B, H, d, P) for
- *                    the partition count P actually used, else
- *                    PA_ERR_WORKSPACE.  Unused when P == 1.
+ *   workspace        NULL = library-owned, fused split as in pa_decode.  Else
+ *                    a device buffer of workspace_bytes >=
+ *                    pa_workspace_bytes(B, H, d, P) for the partition
+ *                    count P actually used (else PA_ERR_WORKSPACE); then the
+ *                    split kernel and a separate merge kernel run (no tickets,
+ *                    so the buffer needs no initialisation).  Unused when
+ *                    P == 1.
  */
 int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *block_tables, const int32_t *context_lens, int B, int H, int Hkv,
@@ -118,10 +125,11 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
  * pa_decode_partials runs only the split kernel: for every (b, h) and
  * partition p < P it writes the partition's running max (log2 units, i.e.
  * of scale * log2(e) * q.K), its normaliser and its unnormalised weighted sum
- * of V rows into `workspace` (layout: [B][H][P] float pairs (max, sum),
- * padded to 256 bytes, then [B][H][P][d] float).  An empty partition stores
- * (-1e30, 0, zeros).  pa_merge_partials combines them into out.  num_partitions
- * must be >= 1 and is used as given (P = num_partitions).
+ * of V rows into `workspace`.  Layout: [B][H][P] float pairs (max, sum),
+ * then, from the next 256-byte boundary, [B][H][P][d] float sums.  An empty
+ * partition stores
+ * (-1e30, 0, zeros).  pa_merge_partials combines them into out.
+ * num_partitions must be >= 1 and is used as given (P = num_partitions).
  */
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_tables, const int32_t *context_lens, int B, int H,
@@ -150,7 +158,7 @@ int pa_device_num_cus(int device);
 /* Static text for a return code. */
 const char *pa_strerror(int code);
 
-/* Frees every library-owned workspace (synchronises the devices that own one). */
+/* Frees every library-owned buffer (synchronises the devices that own one). */
 void pa_release(void);
 
 #ifdef __cplusplus

@@ -1,7 +1,7 @@
 // pa_decode.hip -- paged-attention decode step for gfx950 (MI355X), C ABI.
 //
 // What is computed is declared in include/pa_decode.h.  This file holds the
-// three kernels and the host launcher behind that ABI.
+// kernels and the host launcher behind that ABI.
 //
 // Design (one work unit = one (sequence b, kv head kvh) pair, optionally one
 // partition of its context):
@@ -9,11 +9,12 @@
 // * One workgroup per (kvh, b[, partition]) serves all G = H / Hkv query heads
 //   of the group, so each K/V row is read from HBM once per kv head, not once
 //   per query head.
-// * A wave consumes one 16-token physical block per step.  The block id is
-//   wave-uniform (read from a per-wave register copy of the table slice with
-//   readlane), so each K/V load is an SGPR base plus a per-lane 32-bit offset
-//   that never changes: 16-byte loads, 64 contiguous bytes per token for K and
-//   the full 256-byte row per token for V.
+// * A wave consumes one 16-token physical block per step.  Block ids are read
+//   with scalar loads one group of blocks ahead, so they are wave-uniform and
+//   each block gets a raw buffer descriptor (SGPRs) over exactly its live
+//   rows of head kvh; the per-lane offsets never change.  Slots past the
+//   context and -1 blocks fall outside the descriptor's range and read as
+//   zeros without a memory access, so the streaming loop has no branches.
 // * Scores: the 16 tokens x G heads x 128 product is a small dense
 //   contraction, run on the matrix cores: rows = the block's 16 tokens,
 //   columns = the G query heads repeated to 16, reduction = head_dim.  Each
@@ -26,14 +27,13 @@
 // * V accumulate on the vector ALUs in fp32: lane (g, c) holds 8 elements of
 //   the V rows of tokens 4g..4g+3 and accumulates them for all G heads; the
 //   weights of the other heads come from neighbouring lanes by DPP broadcast.
-// * Epilogue: rows, then waves, are merged with the rescale-and-sum rule
-//   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)); a single
-//   pass writes O / L, the split kernel writes (M, L, O) per partition and a
-//   merge kernel applies the same rule across partitions.
-//
-// Masking: tokens past context_len inside the last block get score -inf and a
-// zero V (select, so NaN in unused slots never leaks); blocks whose table entry
-// is negative (or >= num_pool_blocks when that is given) are skipped whole.
+// * Epilogue: the 4 row groups of a wave are merged with permlane swaps, the
+//   waves through LDS, always with the rescale-and-sum rule
+//   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)).  A single
+//   pass writes O / L.  With partitions, each workgroup writes (M, L, O) to
+//   the workspace; then either a separate merge kernel combines them, or (fused
+//   mode) the last workgroup of each (b, kvh) to finish -- found with an atomic
+//   ticket -- combines them with the same rule and writes out.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -54,8 +54,19 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Start value of a running max: finite, so 2^(m - m') never sees inf - inf.
 constexpr float kMaxInit = -1.0e30f;
 
-constexpr int kWavesPerGroup = 4;  // waves per workgroup
-constexpr int kDepth = 2;          // blocks whose loads are in flight per wave
+#ifndef PA_WAVES_PER_GROUP
+#define PA_WAVES_PER_GROUP 4
+#endif
+#ifndef PA_PIPELINE_DEPTH
+#define PA_PIPELINE_DEPTH 2
+#endif
+constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;  // waves per workgroup
+constexpr int kDepth = PA_PIPELINE_DEPTH;           // blocks in flight per wave
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on GFX9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// What a workgroup does with its merged (M, L, O).
+enum Mode { kSingle = 0, kPartials = 1, kFused = 2 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -67,9 +78,10 @@ struct Params {
     const char *v;
     const int32_t *table;
     const int32_t *lens;
-    void *out;          // single pass: [B][H][d] dtype
-    float2 *part_ml;    // split: [B][H][P] (max, sum)
-    float *part_acc;    // split: [B][H][P][d]
+    void *out;          // [B][H][d] dtype (single pass, fused merge)
+    float2 *part_ml;    // [B][H][P] (max, sum)
+    float *part_acc;    // [B][H][P][d]
+    int *counters;      // [B][Hkv] arrival tickets (fused mode), zero between calls
     long long blk_bytes;  // bytes per physical block: block_size * Hkv * d * esize
     long long pool;       // > 0: ids >= pool are skipped
     int tok_bytes;        // bytes between tokens of a block: Hkv * d * esize
@@ -114,9 +126,27 @@ __device__ __forceinline__ float group_bcast(float x) {
     }
 }
 
+// x combined over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48), result in
+// every lane: a swap of the two 32-lane halves, then of neighbouring rows.
+template <typename Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(y);
+    const auto c = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    return across_rows(x, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float rows_max(float x) {
+    return across_rows(x, [](float a, float b) { return fmaxf(a, b); });
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16 bytes of V row -> 8 fp32 (bf16) or the low 4 of them (f32 uses two loads).
+// 16 bytes of a bf16 V row -> 8 fp32.
 __device__ __forceinline__ void unpack_bf16(const u32x4 &w, float *f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -125,19 +155,20 @@ __device__ __forceinline__ void unpack_bf16(const u32x4 &w, float *f) {
     }
 }
 
-template <int DT, int G>
+template <int G>
 struct WaveState {
     float m;           // running max (log2 units) of this lane's (row, head)
     float l;           // running normaliser
     float acc[G][8];   // unnormalised sum of p * V for every head of the group
 };
 
-// One block's scores, softmax update and V accumulation.  rem = live tokens in
-// this block (only looked at when TAIL).
-template <int DT, int G, bool TAIL>
-__device__ __forceinline__ void consume_block(WaveState<DT, G> &st, const u32x4 *kr,
-                                              const u32x4 *vr, const u32x4 *qr, float qk_scale,
-                                              int g, int rem) {
+// One block's scores, softmax update and V accumulation.  nlive = tokens of the
+// block that take part (0..16); K/V slots at or past nlive were read as zeros
+// (they lie outside the block's buffer range), so only their scores need
+// masking.
+template <int DT, int G>
+__device__ __forceinline__ void consume_block(WaveState<G> &st, const u32x4 *kr, const u32x4 *vr,
+                                              const u32x4 *qr, float qk_scale, int g, int nlive) {
     using Geo = Geometry<DT>;
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DT == PA_DTYPE_BF16) {
@@ -156,10 +187,7 @@ __device__ __forceinline__ void consume_block(WaveState<DT, G> &st, const u32x4 
     }
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        s[r] = c[r] * qk_scale;
-        if constexpr (TAIL) s[r] = (4 * g + r < rem) ? s[r] : -INFINITY;
-    }
+    for (int r = 0; r < 4; ++r) s[r] = (4 * g + r < nlive) ? c[r] * qk_scale : -INFINITY;
     const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     const float mn = fmaxf(st.m, bm);
     const float alpha = fast_exp2(st.m - mn);
@@ -187,11 +215,6 @@ __device__ __forceinline__ void consume_block(WaveState<DT, G> &st, const u32x4 
                 vf[4 + j] = __uint_as_float(vr[2 * r + 1][j]);
             }
         }
-        if constexpr (TAIL) {
-            const bool live = 4 * g + r < rem;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
-        }
         static_for<G>([&](auto hc) {
             constexpr int h = decltype(hc)::value;
             const float ph = group_bcast<G, h>(p[r]);
@@ -208,12 +231,83 @@ __device__ __forceinline__ int acc_elem(int c16, int e) {
     else return 64 * (e / 4) + 4 * c16 + (e % 4);
 }
 
-__device__ __forceinline__ void store_out(void *out, long long idx, float x, int dt) {
-    if (dt == PA_DTYPE_BF16) static_cast<__bf16 *>(out)[idx] = static_cast<__bf16>(x);
-    else static_cast<float *>(out)[idx] = x;
+template <int DT>
+__device__ __forceinline__ void store_pair(void *out, long long idx, float x0, float x1) {
+    if constexpr (DT == PA_DTYPE_BF16) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        bf16x2 v = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+        *reinterpret_cast<bf16x2 *>(static_cast<__bf16 *>(out) + idx) = v;
+    } else {
+        *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) = make_float2(x0, x1);
+    }
 }
 
-template <int DT, int G, int NW, int D>
+// Raw buffer descriptor over [base, base + nbytes): loads at offsets >= nbytes
+// return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char *base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, nbytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Float pair access at agent scope.  The split kernel's fused merge exchanges
+// partials between workgroups that may run on different XCDs (each with its own
+// L2): these stores write through to the device-coherent level and these loads
+// read from it, so no L2 writeback or invalidate is needed.
+__device__ __forceinline__ void store_pair_coherent(float *p, float x0, float x1) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
+                       __builtin_bit_cast(unsigned long long, make_float2(x0, x1)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_pair_coherent(const float *p) {
+    return __builtin_bit_cast(
+        float2, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_pair(const float *p) {
+    if constexpr (COHERENT) return load_pair_coherent(p);
+    else return *reinterpret_cast<const float2 *>(p);
+}
+
+// Combine the P partitions of (b, h) for head-dim elements e, e + 1 with the
+// rescale-and-sum rule, running over the partitions in order.  ml points at
+// the (max, sum) pairs of (b, h), acc at element e of its first partition.
+// Returns the normalised pair (zeros when no partition saw a live token).
+template <bool COHERENT>
+__device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float *acc, int P) {
+    float M = kMaxInit, L = 0.f, o0 = 0.f, o1 = 0.f;
+    constexpr int kUnroll = 8;
+    auto step = [&](float2 s, float2 a) {
+        const float mn = fmaxf(M, s.x);
+        const float fo = fast_exp2(M - mn), fp = fast_exp2(s.x - mn);
+        L = L * fo + s.y * fp;
+        o0 = o0 * fo + a.x * fp;
+        o1 = o1 * fo + a.y * fp;
+        M = mn;
+    };
+    int q = 0;
+    for (; q + kUnroll <= P; q += kUnroll) {
+        float2 s[kUnroll], a[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            s[j] = load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q + j));
+            a[j] = load_pair<COHERENT>(acc + (long long)(q + j) * kHeadDim);
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) step(s[j], a[j]);
+    }
+    for (; q < P; ++q)
+        step(load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q)),
+             load_pair<COHERENT>(acc + (long long)q * kHeadDim));
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    return make_float2(o0 * inv, o1 * inv);
+}
+
+template <int DT, int G, int NW, int D, int MODE>
 __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     using Geo = Geometry<DT>;
     constexpr int KL = Geo::kKLoads, VL = Geo::kVLoads, VPT = VL / 4;
@@ -222,33 +316,50 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const int kvh = wg % p.Hkv;
     const int b = (wg / p.Hkv) % p.B;
     const int part = wg / (p.Hkv * p.B);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
     const int lane = threadIdx.x % kWave;
     const int c16 = lane & 15;  // MFMA column / token of the block for K
     const int g = lane >> 4;    // MFMA row group: tokens 4g..4g+3 for V
 
-    int ctx = p.lens[b];
-    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks * kBlockTokens ? p.max_blocks * kBlockTokens : ctx);
-    const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
     const int lo = part * p.bpp;
-    const int hi = min(lo + p.bpp, nblk);
+    const int first = lo + wave;  // this wave's blocks: first, first + NW, ...
+    const int32_t *trow = p.table + (long long)b * p.max_blocks;
+    // Table entry slot of the wave's i-th block, clamped into the row so the
+    // read is always in bounds (entries past the context are read, never used).
+    auto table_at = [&](int i) -> int {
+        const int j = first + NW * i;
+        return trow[j < p.max_blocks ? j : p.max_blocks - 1];
+    };
 
+    // Independent loads first: the context length, the first group's table
+    // entries and the query all leave before any of them is waited for.
+    int ctx = p.lens[b];
+    int raw0[D];
+#pragma unroll
+    for (int s = 0; s < D; ++s) raw0[s] = table_at(s);
     // B operand: the query of head kvh*G + c16%G, chunk (4m + g) of 16 bytes.
     const char *qrow = p.q + ((long long)b * p.H + kvh * G + (c16 % G)) * (kHeadDim * Geo::kEs);
     u32x4 qr[KL];
 #pragma unroll
     for (int m = 0; m < KL; ++m) qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
 
-    const int head_off = kvh * kHeadDim * Geo::kEs;
-    const int koff = c16 * p.tok_bytes + head_off + 16 * g;
-    int voff[VL];
+    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks * kBlockTokens ? p.max_blocks * kBlockTokens : ctx);
+    const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
+    const int hi = min(lo + p.bpp, nblk);
+    const int nw = hi > first ? (hi - first + NW - 1) / NW : 0;
+
+    // Per-lane byte offsets inside one block's rows of head kvh; never change.
+    const unsigned koff = c16 * p.tok_bytes + 16 * g;
+    unsigned voff[VL];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int s = 0; s < VPT; ++s)
-            voff[r * VPT + s] = (4 * g + r) * p.tok_bytes + head_off + 16 * c16 + 256 * s;
+            voff[r * VPT + s] = (4 * g + r) * p.tok_bytes + 16 * c16 + 256 * s;
+    const char *kbase = p.k + kvh * kHeadDim * Geo::kEs;
+    const char *vbase = p.v + kvh * kHeadDim * Geo::kEs;
 
-    WaveState<DT, G> st;
+    WaveState<G> st;
     st.m = kMaxInit;
     st.l = 0.f;
 #pragma unroll
@@ -256,53 +367,50 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
 
-    const int first = lo + wave;  // this wave's blocks: first, first + NW, ...
-    const int nw = hi > first ? (hi - first + NW - 1) / NW : 0;
-    const int32_t *trow = p.table + (long long)b * p.max_blocks;
+    // Live tokens of the wave's i-th block given its table entry: 0 past the
+    // wave's range and for -1 (or out-of-pool) entries.
+    auto live_tokens = [&](int i, int id) -> int {
+        const int j = first + NW * i;
+        if (j >= hi || id < 0 || (p.pool > 0 && id >= p.pool)) return 0;
+        const int rem = ctx - j * kBlockTokens;
+        return rem < kBlockTokens ? rem : kBlockTokens;
+    };
+    auto issue = [&](u32x4 *kd, u32x4 *vd, int id, int nlive) {
+        const long long off = nlive > 0 ? (long long)id * p.blk_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off, nlive * p.tok_bytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off, nlive * p.tok_bytes);
+#pragma unroll
+        for (int m = 0; m < KL; ++m) kd[m] = load16(rk, koff + 64 * m);
+#pragma unroll
+        for (int n = 0; n < VL; ++n) vd[n] = load16(rv, voff[n]);
+    };
 
-    for (int c0 = 0; c0 < nw; c0 += kWave) {
-        const int cnt = min(kWave, nw - c0);
-        const int tbl = lane < cnt ? trow[first + NW * (c0 + lane)] : -1;
-
+    if (nw > 0) {
+        // D blocks in flight: slot s of group k holds the wave's block kD + s.
         u32x4 kr[D][KL], vr[D][VL];
-        auto live_block = [&](int blk) { return blk >= 0 && (p.pool <= 0 || blk < p.pool); };
-        auto issue = [&](u32x4 *kd, u32x4 *vd, int i) {
-            const int blk = __builtin_amdgcn_readlane(tbl, i);
-            if (!live_block(blk)) return;
-            const char *kb = p.k + (long long)blk * p.blk_bytes;
-            const char *vb = p.v + (long long)blk * p.blk_bytes;
+        int nl[D];
 #pragma unroll
-            for (int m = 0; m < KL; ++m) kd[m] = *reinterpret_cast<const u32x4 *>(kb + koff + 64 * m);
+        for (int s = 0; s < D; ++s) {
+            nl[s] = live_tokens(s, raw0[s]);
+            issue(kr[s], vr[s], raw0[s], nl[s]);
+        }
+        const int ngroups = (nw + D - 1) / D;
+        for (int k = 0; k < ngroups; ++k) {
+            int nid[D];
 #pragma unroll
-            for (int n = 0; n < VL; ++n) vd[n] = *reinterpret_cast<const u32x4 *>(vb + voff[n]);
-        };
-
-#pragma unroll
-        for (int s = 0; s < D; ++s)
-            if (s < cnt) issue(kr[s], vr[s], s);
-
-        for (int i0 = 0; i0 < cnt; i0 += D) {
+            for (int s = 0; s < D; ++s) nid[s] = table_at((k + 1) * D + s);
 #pragma unroll
             for (int s = 0; s < D; ++s) {
-                const int i = i0 + s;
-                if (i < cnt) {
-                    const int blk = __builtin_amdgcn_readlane(tbl, i);
-                    if (live_block(blk)) {
-                        const int rem = ctx - (first + NW * (c0 + i)) * kBlockTokens;
-                        if (rem < kBlockTokens)
-                            consume_block<DT, G, true>(st, kr[s], vr[s], qr, p.qk_scale, g, rem);
-                        else
-                            consume_block<DT, G, false>(st, kr[s], vr[s], qr, p.qk_scale, g, rem);
-                    }
-                    if (i + D < cnt) issue(kr[s], vr[s], i + D);
-                }
+                consume_block<DT, G>(st, kr[s], vr[s], qr, p.qk_scale, g, nl[s]);
+                nl[s] = live_tokens((k + 1) * D + s, nid[s]);
+                issue(kr[s], vr[s], nid[s], nl[s]);
             }
         }
     }
 
-    // ---- merge the 4 row groups of the wave: lanes 16g + c16 share c16 ------
+    // ---- merge the 4 row groups of the wave -----------------------------------
     // The (m, l) of row g and head h sit in the lanes of row g whose column is
-    // h modulo G; fetch them for every head of the group.
+    // h modulo G; after the merge every row holds the same totals.
     float mh[G], lh[G];
     static_for<G>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
@@ -311,24 +419,15 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     });
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float M = fmaxf(mh[h], __shfl_xor(mh[h], 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
+        const float M = rows_max(mh[h]);
         const float f = fast_exp2(mh[h] - M);
-        float L = lh[h] * f;
-        L += __shfl_xor(L, 16);
-        L += __shfl_xor(L, 32);
+        lh[h] = rows_sum(lh[h] * f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = st.acc[h][e] * f;
-            a += __shfl_xor(a, 16);
-            a += __shfl_xor(a, 32);
-            st.acc[h][e] = a;
-        }
+        for (int e = 0; e < 8; ++e) st.acc[h][e] = rows_sum(st.acc[h][e] * f);
         mh[h] = M;
-        lh[h] = L;
     }
 
-    // ---- merge the waves through LDS ----------------------------------------
+    // ---- merge the waves through LDS ------------------------------------------
     __shared__ float2 sm_ml[NW][G];
     __shared__ float sm_acc[NW][G][kHeadDim];
     if (lane < 16) {
@@ -343,24 +442,59 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += NW * kWave) {
-        const int h = idx / kHeadDim, e = idx % kHeadDim;
+    // Thread t handles head h = idx / 64 and elements 2 (idx % 64) + {0, 1}.
+    for (int idx = threadIdx.x; idx < G * (kHeadDim / 2); idx += NW * kWave) {
+        const int h = idx / (kHeadDim / 2), e = 2 * (idx % (kHeadDim / 2));
         float M = kMaxInit;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][h].x);
-        float L = 0.f, O = 0.f;
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float f = fast_exp2(sm_ml[w][h].x - M);
             L = fmaf(sm_ml[w][h].y, f, L);
-            O = fmaf(sm_acc[w][h][e], f, O);
+            o0 = fmaf(sm_acc[w][h][e], f, o0);
+            o1 = fmaf(sm_acc[w][h][e + 1], f, o1);
         }
         const long long bh = (long long)b * p.H + kvh * G + h;
-        if (p.part_acc == nullptr) {
-            store_out(p.out, bh * kHeadDim + e, L > 0.f ? O / L : 0.f, DT);
-        } else {
-            p.part_acc[(bh * p.P + part) * kHeadDim + e] = O;
+        if constexpr (MODE == kSingle) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            store_pair<DT>(p.out, bh * kHeadDim + e, o0 * inv, o1 * inv);
+        } else if constexpr (MODE == kPartials) {
+            *reinterpret_cast<float2 *>(p.part_acc + (bh * p.P + part) * kHeadDim + e) =
+                make_float2(o0, o1);
             if (e == 0) p.part_ml[bh * p.P + part] = make_float2(M, L);
+        } else {
+            store_pair_coherent(p.part_acc + (bh * p.P + part) * kHeadDim + e, o0, o1);
+            if (e == 0)
+                store_pair_coherent(reinterpret_cast<float *>(p.part_ml + bh * p.P + part), M, L);
+        }
+    }
+
+    if constexpr (MODE == kFused) {
+        // Publish this partition (its coherent stores complete before the
+        // barrier), take a ticket; the last of the P workgroups of (b, kvh)
+        // merges all partitions and resets the ticket for the next call.
+        __shared__ int sm_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int prev = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == p.P - 1;
+        }
+        __syncthreads();
+        if (sm_last) {
+            for (int idx = threadIdx.x; idx < G * (kHeadDim / 2); idx += NW * kWave) {
+                const int h = idx / (kHeadDim / 2), e = 2 * (idx % (kHeadDim / 2));
+                const long long bh = (long long)b * p.H + kvh * G + h;
+                const float2 o = merge_partitions<true>(p.part_ml + bh * p.P,
+                                                        p.part_acc + bh * p.P * kHeadDim + e, p.P);
+                store_pair<DT>(p.out, bh * kHeadDim + e, o.x, o.y);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(p.counters + b * p.Hkv + kvh, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -372,48 +506,14 @@ struct MergeParams {
     int B, H, P;
 };
 
-// One wave per (b, h): rescale every partition to the global max and sum.
+// One wave per (b, h); lane l produces elements 2l, 2l + 1.
 template <int DT>
 __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
-    extern __shared__ float sm_w[];  // P weights
     const long long bh = blockIdx.x;
-    const int lane = threadIdx.x;
-    const float2 *ml = mp.part_ml + bh * mp.P;
-    float M = kMaxInit;
-    for (int q = lane; q < mp.P; q += kWave) M = fmaxf(M, ml[q].x);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.f;
-    for (int q = lane; q < mp.P; q += kWave) {
-        const float2 x = ml[q];
-        const float f = fast_exp2(x.x - M);
-        sm_w[q] = f;
-        L = fmaf(x.y, f, L);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    __syncthreads();
-    const float *acc = mp.part_acc + bh * mp.P * kHeadDim + 2 * lane;
-    float o0 = 0.f, o1 = 0.f;
-    int q = 0;
-    for (; q + 4 <= mp.P; q += 4) {
-        float2 a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const float2 *>(acc + (q + j) * kHeadDim);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o0 = fmaf(a[j].x, sm_w[q + j], o0);
-            o1 = fmaf(a[j].y, sm_w[q + j], o1);
-        }
-    }
-    for (; q < mp.P; ++q) {
-        const float2 a = *reinterpret_cast<const float2 *>(acc + q * kHeadDim);
-        o0 = fmaf(a.x, sm_w[q], o0);
-        o1 = fmaf(a.y, sm_w[q], o1);
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    store_out(mp.out, bh * kHeadDim + 2 * lane, o0 * inv, DT);
-    store_out(mp.out, bh * kHeadDim + 2 * lane + 1, o1 * inv, DT);
+    const int e = 2 * threadIdx.x;
+    const float2 o = merge_partitions<false>(mp.part_ml + bh * mp.P,
+                                             mp.part_acc + bh * mp.P * kHeadDim + e, mp.P);
+    store_pair<DT>(mp.out, bh * kHeadDim + e, o.x, o.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -423,9 +523,20 @@ __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
 constexpr int kMinBlocksPerPartition = 8;
 constexpr int kMaxPartitions = 4096;
 
-size_t ml_region_bytes(int B, int H, int P) {
-    size_t bytes = (size_t)B * H * P * sizeof(float2);
-    return (bytes + 255) & ~(size_t)255;
+size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+// Workspace layout: [B][H][P] float2 (max, sum) | [B][H][P][d] float partial
+// sums, the second region starting on a 256-byte boundary.
+struct Layout {
+    size_t ml, acc, total;
+};
+
+Layout workspace_layout(int B, int H, int P) {
+    Layout l;
+    l.ml = 0;
+    l.acc = round256((size_t)B * H * P * sizeof(float2));
+    l.total = l.acc + (size_t)B * H * P * kHeadDim * sizeof(float);
+    return l;
 }
 
 bool aligned(const void *ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -470,8 +581,19 @@ int validate(void *out, const void *q, const void *k_cache, const void *v_cache,
 }
 
 std::mutex g_mutex;
-std::map<int, int> g_cus;                                  // device -> CU count
-std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_workspace;
+std::map<int, int> g_cus;  // device -> CU count
+
+// Library-owned buffers per (device, stream): the partials, and the arrival
+// tickets of the fused split.  The tickets live in a buffer of their own,
+// zeroed when it is (re)allocated; every fused call leaves the tickets it used
+// at zero and nothing else writes there, so they are zero between calls.
+struct LibBuffers {
+    void *partials = nullptr;
+    size_t partial_bytes = 0;
+    int *tickets = nullptr;
+    size_t num_tickets = 0;
+};
+std::map<std::pair<int, hipStream_t>, LibBuffers> g_buffers;
 
 int current_device(int *dev) {
     if (hipGetDevice(dev) != hipSuccess) return PA_ERR_DEVICE;
@@ -493,68 +615,87 @@ int device_cus(int dev) {
     return cus;
 }
 
-int library_workspace(int dev, hipStream_t stream, size_t bytes, void **ptr) {
+int library_buffers(int dev, hipStream_t stream, size_t partial_bytes, size_t num_tickets,
+                    void **partials, int **tickets) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    auto &slot = g_workspace[{dev, stream}];
-    if (slot.second < bytes) {
-        if (slot.first) {
-            // the previous buffer may still be in use by work on this stream
-            if (hipStreamSynchronize(stream) != hipSuccess) return PA_ERR_HIP;
-            if (hipFree(slot.first) != hipSuccess) return PA_ERR_HIP;
-            slot = {nullptr, 0};
-        }
-        void *p = nullptr;
-        if (hipMalloc(&p, bytes) != hipSuccess) return PA_ERR_HIP;
-        slot = {p, bytes};
+    LibBuffers &lb = g_buffers[{dev, stream}];
+    if (lb.partial_bytes < partial_bytes || lb.num_tickets < num_tickets) {
+        // the previous buffers may still be in use by work on this stream
+        if ((lb.partials || lb.tickets) && hipStreamSynchronize(stream) != hipSuccess)
+            return PA_ERR_HIP;
     }
-    *ptr = slot.first;
+    if (lb.partial_bytes < partial_bytes) {
+        if (lb.partials && hipFree(lb.partials) != hipSuccess) return PA_ERR_HIP;
+        lb.partials = nullptr;
+        lb.partial_bytes = 0;
+        if (hipMalloc(&lb.partials, partial_bytes) != hipSuccess) return PA_ERR_HIP;
+        lb.partial_bytes = partial_bytes;
+    }
+    if (lb.num_tickets < num_tickets) {
+        if (lb.tickets && hipFree(lb.tickets) != hipSuccess) return PA_ERR_HIP;
+        lb.tickets = nullptr;
+        lb.num_tickets = 0;
+        if (hipMalloc(&lb.tickets, num_tickets * sizeof(int)) != hipSuccess) return PA_ERR_HIP;
+        if (hipMemset(lb.tickets, 0, num_tickets * sizeof(int)) != hipSuccess) return PA_ERR_HIP;
+        lb.num_tickets = num_tickets;
+    }
+    *partials = lb.partials;
+    *tickets = lb.tickets;
     return PA_OK;
 }
 
-template <int DT, int G>
+template <int DT, int G, int MODE>
 hipError_t launch_main(const Params &p, int groups, hipStream_t stream) {
-    hipLaunchKernelGGL((pa_decode_kernel<DT, G, kWavesPerGroup, kDepth>), dim3(groups),
+    hipLaunchKernelGGL((pa_decode_kernel<DT, G, kWavesPerGroup, kDepth, MODE>), dim3(groups),
                        dim3(kWavesPerGroup * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, int MODE>
 hipError_t dispatch_g(const Params &p, int G, int groups, hipStream_t stream) {
     switch (G) {
-        case 1: return launch_main<DT, 1>(p, groups, stream);
-        case 2: return launch_main<DT, 2>(p, groups, stream);
-        case 4: return launch_main<DT, 4>(p, groups, stream);
-        case 8: return launch_main<DT, 8>(p, groups, stream);
-        default: return launch_main<DT, 16>(p, groups, stream);
+        case 1: return launch_main<DT, 1, MODE>(p, groups, stream);
+        case 2: return launch_main<DT, 2, MODE>(p, groups, stream);
+        case 4: return launch_main<DT, 4, MODE>(p, groups, stream);
+        case 8: return launch_main<DT, 8, MODE>(p, groups, stream);
+        default: return launch_main<DT, 16, MODE>(p, groups, stream);
     }
 }
 
-int run_main(const Params &p, int dtype, int G, hipStream_t stream) {
+template <int DT>
+hipError_t dispatch_mode(const Params &p, int G, int mode, int groups, hipStream_t stream) {
+    switch (mode) {
+        case kSingle: return dispatch_g<DT, kSingle>(p, G, groups, stream);
+        case kPartials: return dispatch_g<DT, kPartials>(p, G, groups, stream);
+        default: return dispatch_g<DT, kFused>(p, G, groups, stream);
+    }
+}
+
+int run_main(const Params &p, int dtype, int G, int mode, hipStream_t stream) {
     const long long groups = (long long)p.Hkv * p.B * p.P;
     if (groups > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     const hipError_t e = dtype == PA_DTYPE_BF16
-                             ? dispatch_g<PA_DTYPE_BF16>(p, G, (int)groups, stream)
-                             : dispatch_g<PA_DTYPE_F32>(p, G, (int)groups, stream);
+                             ? dispatch_mode<PA_DTYPE_BF16>(p, G, mode, (int)groups, stream)
+                             : dispatch_mode<PA_DTYPE_F32>(p, G, mode, (int)groups, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-int run_merge(void *out, const void *ws, int B, int H, int P, int dtype, hipStream_t stream) {
+int run_merge(void *out, void *ws, int B, int H, int P, int dtype, hipStream_t stream) {
+    const Layout l = workspace_layout(B, H, P);
     MergeParams mp;
-    mp.part_ml = static_cast<const float2 *>(ws);
-    mp.part_acc = reinterpret_cast<const float *>(static_cast<const char *>(ws) +
-                                                  ml_region_bytes(B, H, P));
+    mp.part_ml = reinterpret_cast<const float2 *>(static_cast<char *>(ws) + l.ml);
+    mp.part_acc = reinterpret_cast<const float *>(static_cast<char *>(ws) + l.acc);
     mp.out = out;
     mp.B = B;
     mp.H = H;
     mp.P = P;
     const long long groups = (long long)B * H;
     if (groups > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-    const size_t lds = (size_t)P * sizeof(float);
     if (dtype == PA_DTYPE_BF16)
-        hipLaunchKernelGGL(pa_merge_kernel<PA_DTYPE_BF16>, dim3((int)groups), dim3(kWave), lds,
+        hipLaunchKernelGGL(pa_merge_kernel<PA_DTYPE_BF16>, dim3((int)groups), dim3(kWave), 0,
                            stream, mp);
     else
-        hipLaunchKernelGGL(pa_merge_kernel<PA_DTYPE_F32>, dim3((int)groups), dim3(kWave), lds,
+        hipLaunchKernelGGL(pa_merge_kernel<PA_DTYPE_F32>, dim3((int)groups), dim3(kWave), 0,
                            stream, mp);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -571,6 +712,7 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.out = nullptr;
     p.part_ml = nullptr;
     p.part_acc = nullptr;
+    p.counters = nullptr;
     p.tok_bytes = Hkv * kHeadDim * esize;
     p.blk_bytes = (long long)kBlockTokens * p.tok_bytes;
     p.pool = pool;
@@ -582,6 +724,13 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.bpp = (max_blocks + P - 1) / P;
     p.qk_scale = scale * kLog2e;
     return p;
+}
+
+void attach_workspace(Params &p, void *ws) {
+    const Layout l = workspace_layout(p.B, p.H, p.P);
+    char *base = static_cast<char *>(ws);
+    p.part_ml = reinterpret_cast<float2 *>(base + l.ml);
+    p.part_acc = reinterpret_cast<float *>(base + l.acc);
 }
 
 int even_partitions(int max_blocks, int P) {
@@ -609,8 +758,7 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
 
 size_t pa_workspace_bytes(int B, int H, int d, int num_partitions) {
     if (B <= 0 || H <= 0 || d <= 0 || num_partitions <= 1) return 0;
-    return ml_region_bytes(B, H, num_partitions) +
-           (size_t)B * H * num_partitions * d * sizeof(float);
+    return workspace_layout(B, H, num_partitions).total;
 }
 
 int pa_device_num_cus(int device) { return device_cus(device); }
@@ -658,21 +806,22 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     if (P > kMaxPartitions) return PA_ERR_UNSUPPORTED;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv,
                            max_blocks, scale, v.esize, num_pool_blocks, P);
-    if (P == 1) {
-        p.out = out;
-        return run_main(p, dtype, v.G, s);
-    }
-    const size_t need = pa_workspace_bytes(B, H, d, P);
-    void *ws = workspace;
-    if (ws) {
+    p.out = out;
+    if (P == 1) return run_main(p, dtype, v.G, kSingle, s);
+    const size_t need = workspace_layout(B, H, P).total;
+    if (workspace) {
+        // caller workspace: split kernel, then the merge kernel (no tickets)
         if (workspace_bytes < need) return PA_ERR_WORKSPACE;
-    } else if ((rc = library_workspace(dev, s, need, &ws)) != PA_OK) {
-        return rc;
+        attach_workspace(p, workspace);
+        if ((rc = run_main(p, dtype, v.G, kPartials, s)) != PA_OK) return rc;
+        return run_merge(out, workspace, B, H, P, dtype, s);
     }
-    p.part_ml = static_cast<float2 *>(ws);
-    p.part_acc = reinterpret_cast<float *>(static_cast<char *>(ws) + ml_region_bytes(B, H, P));
-    if ((rc = run_main(p, dtype, v.G, s)) != PA_OK) return rc;
-    return run_merge(out, ws, B, H, P, dtype, s);
+    void *ws = nullptr;
+    int *tickets = nullptr;
+    if ((rc = library_buffers(dev, s, need, (size_t)B * Hkv, &ws, &tickets)) != PA_OK) return rc;
+    attach_workspace(p, ws);
+    p.counters = tickets;
+    return run_main(p, dtype, v.G, kFused, s);
 }
 
 int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -697,14 +846,11 @@ int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
     if (!workspace) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
     const int P = num_partitions;
-    const size_t need = ml_region_bytes(B, H, P) + (size_t)B * H * P * d * sizeof(float);
-    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (workspace_bytes < workspace_layout(B, H, P).total) return PA_ERR_WORKSPACE;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv,
                            max_blocks, scale, v.esize, num_pool_blocks, P);
-    p.part_ml = static_cast<float2 *>(workspace);
-    p.part_acc =
-        reinterpret_cast<float *>(static_cast<char *>(workspace) + ml_region_bytes(B, H, P));
-    return run_main(p, dtype, v.G, static_cast<hipStream_t>(stream));
+    attach_workspace(p, workspace);
+    return run_main(p, dtype, v.G, kPartials, static_cast<hipStream_t>(stream));
 }
 
 int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, int B, int H,
@@ -719,25 +865,25 @@ int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, 
     if (!workspace) return PA_ERR_WORKSPACE;
     if (!aligned(out, 16) || !aligned(workspace, 16)) return PA_ERR_ALIGN;
     const int P = num_partitions;
-    const size_t need = ml_region_bytes(B, H, P) + (size_t)B * H * P * d * sizeof(float);
+    const size_t need = workspace_layout(B, H, P).total;
     if (workspace_bytes < need) return PA_ERR_WORKSPACE;
     const size_t esize = dtype == PA_DTYPE_BF16 ? 2 : 4;
     if (overlaps(out, (size_t)B * H * d * esize, workspace, need)) return PA_ERR_ALIAS;
-    return run_merge(out, workspace, B, H, P, dtype, static_cast<hipStream_t>(stream));
+    return run_merge(out, const_cast<void *>(workspace), B, H, P, dtype,
+                     static_cast<hipStream_t>(stream));
 }
 
 void pa_release(void) {
     std::lock_guard<std::mutex> lock(g_mutex);
     int prev = -1;
     const bool have_prev = hipGetDevice(&prev) == hipSuccess;
-    for (auto &kv : g_workspace) {
-        if (!kv.second.first) continue;
-        if (hipSetDevice(kv.first.first) == hipSuccess) {
-            (void)hipDeviceSynchronize();
-            (void)hipFree(kv.second.first);
-        }
+    for (auto &kv : g_buffers) {
+        if (hipSetDevice(kv.first.first) != hipSuccess) continue;
+        (void)hipDeviceSynchronize();
+        if (kv.second.partials) (void)hipFree(kv.second.partials);
+        if (kv.second.tickets) (void)hipFree(kv.second.tickets);
     }
-    g_workspace.clear();
+    g_buffers.clear();
     if (have_prev) (void)hipSetDevice(prev);
 }
 

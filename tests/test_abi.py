@@ -149,6 +149,8 @@ def test_ex_and_split_half_validation():
     assert lib.pa_merge_partials(0x700000 + 64, 0x700000, need, 1, 32, 128, 4, 1, None) == \
         pa.PA_ERR_ALIAS
     assert lib.pa_merge_partials(FAKE["out"], 0x700000, need, 0, 32, 128, 4, 1, None) == pa.PA_OK
+    assert lib.pa_merge_partials(FAKE["out"], 0x700000, need, 1, 0, 128, 4, 1, None) == \
+        pa.PA_ERR_SHAPE
 
 
 def test_binding_rejects_bad_tensors():
