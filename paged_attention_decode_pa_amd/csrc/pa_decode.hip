@@ -277,34 +277,45 @@ __device__ __forceinline__ float2 load_pair(const float *p) {
 // rescale-and-sum rule, running over the partitions in order.  ml points at
 // the (max, sum) pairs of (b, h), acc at element e of its first partition.
 // Returns the normalised pair (zeros when no partition saw a live token).
-template <bool COHERENT>
-__device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float *acc, int P) {
+// All loads of a chunk of CHUNK partitions leave before the first is used.
+// Reads past P are clamped to the last partition and replaced by an empty
+// partition (max -1e30, sum 0, zeros), which leaves the running state as it is.
+template <int CHUNK, bool COHERENT>
+__device__ __forceinline__ float2 merge_chunked(const float2 *ml, const float *acc, int P) {
     float M = kMaxInit, L = 0.f, o0 = 0.f, o1 = 0.f;
-    constexpr int kUnroll = 8;
-    auto step = [&](float2 s, float2 a) {
-        const float mn = fmaxf(M, s.x);
-        const float fo = fast_exp2(M - mn), fp = fast_exp2(s.x - mn);
-        L = L * fo + s.y * fp;
-        o0 = o0 * fo + a.x * fp;
-        o1 = o1 * fo + a.y * fp;
-        M = mn;
-    };
-    int q = 0;
-    for (; q + kUnroll <= P; q += kUnroll) {
-        float2 s[kUnroll], a[kUnroll];
+    for (int q0 = 0; q0 < P; q0 += CHUNK) {
+        float2 s[CHUNK], a[CHUNK];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            s[j] = load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q + j));
-            a[j] = load_pair<COHERENT>(acc + (long long)(q + j) * kHeadDim);
+        for (int j = 0; j < CHUNK; ++j) {
+            const int q = q0 + j < P ? q0 + j : P - 1;
+            s[j] = load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q));
+            a[j] = load_pair<COHERENT>(acc + (long long)q * kHeadDim);
         }
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) step(s[j], a[j]);
+        for (int j = 0; j < CHUNK; ++j) {
+            const bool live = q0 + j < P;
+            s[j] = live ? s[j] : make_float2(kMaxInit, 0.f);
+            a[j] = live ? a[j] : make_float2(0.f, 0.f);
+            const float mn = fmaxf(M, s[j].x);
+            const float fo = fast_exp2(M - mn), fp = fast_exp2(s[j].x - mn);
+            L = L * fo + s[j].y * fp;
+            o0 = o0 * fo + a[j].x * fp;
+            o1 = o1 * fo + a[j].y * fp;
+            M = mn;
+        }
     }
-    for (; q < P; ++q)
-        step(load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q)),
-             load_pair<COHERENT>(acc + (long long)q * kHeadDim));
     const float inv = L > 0.f ? 1.f / L : 0.f;
     return make_float2(o0 * inv, o1 * inv);
+}
+
+// The chunk is the smallest of 4, 8, 16, 32 that holds P (32 beyond that), so
+// few partitions do not pay for loads of padding.
+template <bool COHERENT>
+__device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float *acc, int P) {
+    if (P <= 4) return merge_chunked<4, COHERENT>(ml, acc, P);
+    if (P <= 8) return merge_chunked<8, COHERENT>(ml, acc, P);
+    if (P <= 16) return merge_chunked<16, COHERENT>(ml, acc, P);
+    return merge_chunked<32, COHERENT>(ml, acc, P);
 }
 
 template <int DT, int G, int NW, int D, int MODE>
