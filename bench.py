@@ -200,6 +200,22 @@ def measure(cid, dev, steps, warmup, use_graph, num_partitions=0):
     return w, t_step, max_err
 
 
+def recorded_traffic(workload_name):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the kernel source as it is now and on this workload; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "paged_attention_decode_pa_amd", "csrc", "pa_decode.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload_name:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(cid, budget_s):
     import oracle
     import pa_inputs as pi
@@ -307,7 +323,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(c.name),
             "avg_launch_us": round(t_dom * 1e6, 3),
             "launches_per_step": 1,
             "bytes_per_launch": dom_bytes,

@@ -248,8 +248,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, nbytes, kRsrcWord3);
 }
 
+#ifndef PA_KV_CACHE_POLICY
+#define PA_KV_CACHE_POLICY 2
+#endif
+// Cache-policy bits of the K/V stream loads (the buffer instruction's aux field):
+// 2 = non-temporal, so the single-use stream does not evict the table, the
+// query, the partials or the kernel code from the caches.
+constexpr int kKvPolicy = PA_KV_CACHE_POLICY;
+
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kKvPolicy));
 }
 
 // Float pair access at agent scope.  The split kernel's fused merge exchanges
