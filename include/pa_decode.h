@@ -31,8 +31,10 @@
  * nearest even.
  *
  * Conventions:
- *   - Supported shapes: d = 128, block_size = 16, H % Hkv == 0 with
- *     H / Hkv in {1, 2, 4, 8, 16}.  Others return PA_ERR_UNSUPPORTED.
+ *   - Supported shapes: d = 128; block_size a power of two from 16 to 256;
+ *     H % Hkv == 0 with H / Hkv in {1, 2, 4, 8, 16}.  Others return
+ *     PA_ERR_UNSUPPORTED.  Sequences are processed in tiles of 16 tokens; a
+ *     row of the table covers T = max_blocks * block_size / 16 tiles.
  *   - All calls only enqueue work on `stream` (a hipStream_t, NULL = the null
  *     stream); nothing synchronises with the host.  The return code reports
  *     errors the host can see: argument validation (checked before any HIP
@@ -100,8 +102,9 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
 /*
  * pa_decode with the choices exposed.
  *   num_partitions   0 = heuristic (as pa_decode), 1 = single pass, n > 1 =
- *                    split into n partitions (reduced to ceil(max_blocks /
- *                    ceil(max_blocks / n)) so none is empty by construction).
+ *                    split each sequence's T tiles into n partitions of
+ *                    ceil(T / n) tiles (n reduced to ceil(T / ceil(T / n)) so
+ *                    none is empty by construction).
  *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
  *                    treated like -1 instead of being read (a guard against
  *                    out-of-range ids).
@@ -129,6 +132,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
  * then, from the next 256-byte boundary, [B][H][P][d] float sums.  An empty
  * partition stores
  * (-1e30, 0, zeros).  pa_merge_partials combines them into out.
+ * Partition p covers tiles [p * ceil(T / P), (p + 1) * ceil(T / P)).
  * num_partitions must be >= 1 and is used as given (P = num_partitions).
  */
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
@@ -146,9 +150,10 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
  * The launch heuristic (pure; no HIP call).  Work units are the B * Hkv
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
  * they already cover the device (>= num_cus) it returns 1.  Otherwise it
- * splits each unit's context into enough partitions to give about num_cus
- * workgroups, keeping at least 8 blocks of block_size tokens per partition,
- * then evens the partitions out.  Returns >= 1 (1 for non-positive inputs).
+ * splits each unit's T tiles into enough partitions to give about num_cus
+ * workgroups, keeping at least 8 tiles (128 tokens) per partition, then evens
+ * the partitions out.  Returns >= 1 (1 for non-positive inputs or block_size
+ * below 16).
  */
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
 

@@ -48,7 +48,11 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kBlockTokens = 16;  // tokens per physical block (block_size)
+// The kernels walk a sequence in tiles of 16 tokens, the row count of one MFMA
+// tile.  A physical block of block_size tokens (a power of two from 16 to 256)
+// holds block_size / 16 tiles; each tile lies inside one block.
+constexpr int kTile = 16;
+constexpr int kMaxBlockSize = 256;
 constexpr int kHeadDim = 128;     // d
 constexpr float kLog2e = 1.44269504088896340736f;
 // Start value of a running max: finite, so 2^(m - m') never sees inf - inf.
@@ -85,7 +89,10 @@ struct Params {
     long long blk_bytes;  // bytes per physical block: block_size * Hkv * d * esize
     long long pool;       // > 0: ids >= pool are skipped
     int tok_bytes;        // bytes between tokens of a block: Hkv * d * esize
-    int B, H, Hkv, max_blocks, P, bpp;
+    int B, H, Hkv, max_blocks, P;
+    int tiles_log2;       // log2(block_size / 16): tiles per physical block
+    int max_tiles;        // max_blocks * block_size / 16
+    int bpp;              // tiles per partition
     float qk_scale;       // scale * log2(e)
 };
 
@@ -341,13 +348,15 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const int g = lane >> 4;    // MFMA row group: tokens 4g..4g+3 for V
 
     const int lo = part * p.bpp;
-    const int first = lo + wave;  // this wave's blocks: first, first + NW, ...
+    const int first = lo + wave;  // this wave's tiles: first, first + NW, ...
     const int32_t *trow = p.table + (long long)b * p.max_blocks;
-    // Table entry slot of the wave's i-th block, clamped into the row so the
-    // read is always in bounds (entries past the context are read, never used).
+    // Table entry of the block holding the wave's i-th tile, the read clamped
+    // into the row so it always stays in bounds (entries past the context are
+    // read, never used).
+    auto tile_of = [&](int i) -> int { return first + NW * i; };
     auto table_at = [&](int i) -> int {
-        const int j = first + NW * i;
-        return trow[j < p.max_blocks ? j : p.max_blocks - 1];
+        const int e = tile_of(i) >> p.tiles_log2;
+        return trow[e < p.max_blocks ? e : p.max_blocks - 1];
     };
 
     // Independent loads first: the context length, the first group's table
@@ -362,9 +371,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
     for (int m = 0; m < KL; ++m) qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
 
-    ctx = ctx < 0 ? 0 : (ctx > p.max_blocks * kBlockTokens ? p.max_blocks * kBlockTokens : ctx);
-    const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
-    const int hi = min(lo + p.bpp, nblk);
+    ctx = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
+    const int ntiles = (ctx + kTile - 1) / kTile;
+    const int hi = min(lo + p.bpp, ntiles);
     const int nw = hi > first ? (hi - first + NW - 1) / NW : 0;
 
     // Per-lane byte offsets inside one block's rows of head kvh; never change.
@@ -386,16 +395,20 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
 
-    // Live tokens of the wave's i-th block given its table entry: 0 past the
-    // wave's range and for -1 (or out-of-pool) entries.
+    // Live tokens of the wave's i-th tile given its block's table entry: 0 past
+    // the wave's range and for -1 (or out-of-pool) entries.
     auto live_tokens = [&](int i, int id) -> int {
-        const int j = first + NW * i;
+        const int j = tile_of(i);
         if (j >= hi || id < 0 || (p.pool > 0 && id >= p.pool)) return 0;
-        const int rem = ctx - j * kBlockTokens;
-        return rem < kBlockTokens ? rem : kBlockTokens;
+        const int rem = ctx - j * kTile;
+        return rem < kTile ? rem : kTile;
     };
-    auto issue = [&](u32x4 *kd, u32x4 *vd, int id, int nlive) {
-        const long long off = nlive > 0 ? (long long)id * p.blk_bytes : 0;
+    // Loads of the wave's i-th tile: its rows start at the block's base plus
+    // the tile's place inside the block.
+    auto issue = [&](u32x4 *kd, u32x4 *vd, int i, int id, int nlive) {
+        const int in_block = tile_of(i) & ((1 << p.tiles_log2) - 1);
+        const long long off =
+            nlive > 0 ? (long long)id * p.blk_bytes + (long long)in_block * kTile * p.tok_bytes : 0;
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off, nlive * p.tok_bytes);
         const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off, nlive * p.tok_bytes);
 #pragma unroll
@@ -411,7 +424,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             nl[s] = live_tokens(s, raw0[s]);
-            issue(kr[s], vr[s], raw0[s], nl[s]);
+            issue(kr[s], vr[s], s, raw0[s], nl[s]);
         }
         const int ngroups = (nw + D - 1) / D;
         for (int k = 0; k < ngroups; ++k) {
@@ -422,7 +435,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             for (int s = 0; s < D; ++s) {
                 consume_block<DT, G>(st, kr[s], vr[s], qr, p.qk_scale, g, nl[s]);
                 nl[s] = live_tokens((k + 1) * D + s, nid[s]);
-                issue(kr[s], vr[s], nid[s], nl[s]);
+                issue(kr[s], vr[s], (k + 1) * D + s, nid[s], nl[s]);
             }
         }
     }
@@ -539,7 +552,7 @@ __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
 // host side
 // ---------------------------------------------------------------------------
 
-constexpr int kMinBlocksPerPartition = 8;
+constexpr int kMinTilesPerPartition = 8;  // 128 tokens
 constexpr int kMaxPartitions = 4096;
 
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
@@ -579,7 +592,9 @@ int validate(void *out, const void *q, const void *k_cache, const void *v_cache,
     if (H % Hkv != 0) return PA_ERR_SHAPE;
     if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
     if (!std::isfinite(scale)) return PA_ERR_VALUE;
-    if (d != kHeadDim || block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+    if (d != kHeadDim || block_size < kTile || block_size > kMaxBlockSize ||
+        (block_size & (block_size - 1)) != 0)
+        return PA_ERR_UNSUPPORTED;
     const int G = H / Hkv;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PA_ERR_UNSUPPORTED;
     if ((long long)max_blocks * block_size > (1LL << 30)) return PA_ERR_UNSUPPORTED;
@@ -719,9 +734,19 @@ int run_merge(void *out, void *ws, int B, int H, int P, int dtype, hipStream_t s
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int log2_int(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+
+// Tiles of 16 tokens in a table row of max_blocks blocks of block_size tokens.
+int table_tiles(int max_blocks, int block_size) { return max_blocks * (block_size / kTile); }
+
 Params make_params(const void *q, const void *k_cache, const void *v_cache,
                    const int32_t *block_tables, const int32_t *context_lens, int B, int H,
-                   int Hkv, int max_blocks, float scale, int esize, long long pool, int P) {
+                   int Hkv, int max_blocks, int block_size, float scale, int esize,
+                   long long pool, int P) {
     Params p;
     p.q = static_cast<const char *>(q);
     p.k = static_cast<const char *>(k_cache);
@@ -733,14 +758,16 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.part_acc = nullptr;
     p.counters = nullptr;
     p.tok_bytes = Hkv * kHeadDim * esize;
-    p.blk_bytes = (long long)kBlockTokens * p.tok_bytes;
+    p.blk_bytes = (long long)block_size * p.tok_bytes;
     p.pool = pool;
     p.B = B;
     p.H = H;
     p.Hkv = Hkv;
     p.max_blocks = max_blocks;
     p.P = P;
-    p.bpp = (max_blocks + P - 1) / P;
+    p.tiles_log2 = log2_int(block_size / kTile);
+    p.max_tiles = table_tiles(max_blocks, block_size);
+    p.bpp = (p.max_tiles + P - 1) / P;
     p.qk_scale = scale * kLog2e;
     return p;
 }
@@ -752,11 +779,12 @@ void attach_workspace(Params &p, void *ws) {
     p.part_acc = reinterpret_cast<float *>(base + l.acc);
 }
 
-int even_partitions(int max_blocks, int P) {
+// P reduced so that no partition of a row of `tiles` tiles is empty.
+int even_partitions(int tiles, int P) {
     if (P < 1) P = 1;
-    if (P > max_blocks) P = max_blocks;
-    const int bpp = (max_blocks + P - 1) / P;
-    return (max_blocks + bpp - 1) / bpp;
+    if (P > tiles) P = tiles;
+    const int per = (tiles + P - 1) / P;
+    return (tiles + per - 1) / per;
 }
 
 }  // namespace
@@ -764,15 +792,17 @@ int even_partitions(int max_blocks, int P) {
 extern "C" {
 
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {
-    if (B <= 0 || Hkv <= 0 || max_blocks <= 0 || block_size <= 0 || num_cus <= 0) return 1;
+    if (B <= 0 || Hkv <= 0 || max_blocks <= 0 || block_size < kTile || num_cus <= 0) return 1;
     const long long units = (long long)B * Hkv;
     if (units >= num_cus) return 1;
+    const long long tiles = (long long)max_blocks * block_size / kTile;
+    if (tiles > 0x7FFFFFFF) return 1;
     long long P = (num_cus + units - 1) / units;
-    const long long cap = max_blocks / kMinBlocksPerPartition;
+    const long long cap = tiles / kMinTilesPerPartition;
     if (P > cap) P = cap;
     if (P > kMaxPartitions) P = kMaxPartitions;
     if (P < 1) P = 1;
-    return even_partitions(max_blocks, (int)P);
+    return even_partitions((int)tiles, (int)P);
 }
 
 size_t pa_workspace_bytes(int B, int H, int d, int num_partitions) {
@@ -820,11 +850,11 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         if (cus < 0) return cus;
         P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
     } else {
-        P = even_partitions(max_blocks, num_partitions);
+        P = even_partitions(table_tiles(max_blocks, block_size), num_partitions);
     }
     if (P > kMaxPartitions) return PA_ERR_UNSUPPORTED;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv,
-                           max_blocks, scale, v.esize, num_pool_blocks, P);
+                           max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
     p.out = out;
     if (P == 1) return run_main(p, dtype, v.G, kSingle, s);
     const size_t need = workspace_layout(B, H, P).total;
@@ -867,7 +897,7 @@ int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
     const int P = num_partitions;
     if (workspace_bytes < workspace_layout(B, H, P).total) return PA_ERR_WORKSPACE;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv,
-                           max_blocks, scale, v.esize, num_pool_blocks, P);
+                           max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
     attach_workspace(p, workspace);
     return run_main(p, dtype, v.G, kPartials, static_cast<hipStream_t>(stream));
 }

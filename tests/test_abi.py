@@ -36,20 +36,24 @@ def test_strerror_covers_codes():
     assert pa.strerror(-99) == "unknown error code"
 
 
-@pytest.mark.parametrize("B,Hkv,max_blocks,cus,expect", [
-    (2, 8, 4, 256, 1),        # 60 tokens: too short to split (needs 8 blocks/partition)
-    (1, 8, 32, 256, 4),       # 512 tokens: capped at 32 / 8 partitions
-    (16, 8, 16, 256, 2),      # 128 units -> 2 partitions of 8 blocks
-    (4, 8, 128, 256, 8),      # 32 units -> 8 partitions of 16 blocks
-    (1, 8, 1024, 256, 32),    # 8 units -> 32 partitions of 32 blocks
-    (32, 8, 1024, 256, 1),    # 256 units already fill 256 CUs
-    (1, 1, 100, 256, 12),     # capped at 100 // 8 = 12, evened to 12 (9 blocks each)
-    (1, 8, 7, 256, 1),
-    (0, 8, 10, 256, 1),
-    (3, 8, 1000, 0, 1),
+@pytest.mark.parametrize("B,Hkv,max_blocks,bs,cus,expect", [
+    (2, 8, 4, 16, 256, 1),        # 60 tokens: too short to split (needs 8 tiles/partition)
+    (1, 8, 32, 16, 256, 4),       # 512 tokens: capped at 32 / 8 partitions
+    (16, 8, 16, 16, 256, 2),      # 128 units -> 2 partitions of 8 tiles
+    (4, 8, 128, 16, 256, 8),      # 32 units -> 8 partitions of 16 tiles
+    (1, 8, 1024, 16, 256, 32),    # 8 units -> 32 partitions of 32 tiles
+    (32, 8, 1024, 16, 256, 1),    # 256 units already fill 256 CUs
+    (1, 1, 100, 16, 256, 12),     # capped at 100 // 8 = 12, evened to 12 (9 tiles each)
+    (1, 8, 7, 16, 256, 1),
+    (0, 8, 10, 16, 256, 1),
+    (3, 8, 1000, 16, 0, 1),
+    (1, 8, 64, 256, 256, 32),     # 16384 tokens in 256-token blocks: same as 1024 x 16
+    (8, 8, 2, 256, 256, 4),       # 512 tokens, 64 units -> 4 partitions of 8 tiles
+    (1, 8, 16, 32, 256, 4),       # 512 tokens in 32-token blocks
+    (1, 8, 10, 8, 256, 1),        # block_size below 16
 ])
-def test_choose_partitions(B, Hkv, max_blocks, cus, expect):
-    assert pa.pa_choose_partitions(B, Hkv, max_blocks, 16, cus) == expect
+def test_choose_partitions(B, Hkv, max_blocks, bs, cus, expect):
+    assert pa.pa_choose_partitions(B, Hkv, max_blocks, bs, cus) == expect
 
 
 def test_choose_partitions_properties():
@@ -90,7 +94,9 @@ def call(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=64), pa.PA_ERR_UNSUPPORTED),
     (dict(d=256), pa.PA_ERR_UNSUPPORTED),
-    (dict(bs=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=48), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=512), pa.PA_ERR_UNSUPPORTED),
     (dict(H=24, Hkv=8), pa.PA_ERR_UNSUPPORTED),   # G = 3
     (dict(H=32, Hkv=6), pa.PA_ERR_SHAPE),         # H % Hkv != 0
     (dict(B=-1), pa.PA_ERR_SHAPE),
@@ -123,6 +129,8 @@ def test_valid_call_without_device_reports_device_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; the launch path is covered by the GPU tests")
     assert call() == pa.PA_ERR_DEVICE
+    for bs in (16, 32, 64, 128, 256):  # every supported block size passes validation
+        assert call(bs=bs) == pa.PA_ERR_DEVICE
 
 
 def test_ex_and_split_half_validation():

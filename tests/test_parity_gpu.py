@@ -279,3 +279,45 @@ def test_library_workspace_reused_across_shapes(gpu):
         say(f"reuse {i}: B={B} ctx={ctx} Hkv={Hkv} P={parts}")
         out = run_gpu(case, gpu, num_partitions=parts)
         assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"reuse step {i}")
+
+
+BLOCK_SIZE_CASES = [
+    # B, lens, H, Hkv, bs, holes
+    (3, [0, 300, 1000], 32, 8, 256, [(2, 1)]),
+    (5, [1, 255, 256, 257, 700], 16, 8, 256, []),
+    (4, [33, 64, 65, 500], 32, 4, 32, [(3, 5)]),
+    (2, [129, 1500], 32, 8, 64, [(1, 7), (1, 8)]),
+    (2, [4000, 17], 8, 8, 128, [(0, 3)]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", BLOCK_SIZE_CASES)
+@pytest.mark.parametrize("parts", [0, 1, 5])
+def test_block_sizes(gpu, dtype, shape, parts):
+    B, lens, H, Hkv, bs, holes = shape
+    max_blocks = max(math.ceil(n / bs) for n in lens) + 1
+    need = sum(math.ceil(n / bs) for n in lens)
+    case = pi.make_case(B, lens, H, Hkv, 128, bs, dtype=dtype, seed=bs + sum(lens),
+                        max_blocks=max_blocks, pool=need + 3, holes=holes)
+    say(f"block_size {bs} lens {lens} {dtype} P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"bs={bs} P={parts}")
+    poisoned = pi.poison_unused(case)
+    clean = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    clean.block_tables = poisoned.block_tables
+    a = run_gpu(clean, gpu, num_partitions=parts)
+    b = run_gpu(poisoned, gpu, num_partitions=parts)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("seq", [128, 512, 2048])
+def test_script_default_sweep(gpu, B, seq):
+    # benchmark_decoding.py's default sweep: batch sizes 1/8/32 x sequence lengths
+    # 128/512/2048, 16 heads over 8 kv heads, head_dim 128, block_size 256, a
+    # scattered table over a pool of exactly the blocks needed
+    case = pi.make_case(B, seq, 16, 8, 128, 256, dtype="bf16", seed=B * 10000 + seq)
+    say(f"script sweep B={B} seq={seq}")
+    out = run_gpu(case, gpu)
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"sweep B={B} seq={seq}")
