@@ -92,10 +92,12 @@ class Workload:
         self.cus = pa.pa_device_num_cus(dev.index or 0)
         self.P = (pa.pa_choose_partitions(c.batch, c.num_kv_heads, c.max_blocks, c.block_size,
                                           self.cus) if num_partitions == 0
-                  else min(num_partitions, c.max_blocks))
+                  else num_partitions)
+        tiles = c.max_blocks * c.block_size // 16   # partitions split 16-token tiles
+        self.P = min(self.P, tiles)
         if self.P > 1:
-            bpp = math.ceil(c.max_blocks / self.P)
-            self.P = math.ceil(c.max_blocks / bpp)
+            per = math.ceil(tiles / self.P)
+            self.P = math.ceil(tiles / per)
         self.num_partitions = num_partitions
         self.lib = pa.load()
 
@@ -200,15 +202,27 @@ def measure(cid, dev, steps, warmup, use_graph, num_partitions=0):
     return w, t_step, max_err
 
 
+def kernel_source_sha256():
+    """One digest over the library's sources: every file under csrc/ (sorted by
+    name, each name followed by its bytes) and the C header."""
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_attention_decode_pa_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files.append(os.path.join(ROOT, "include", "pa_decode.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def recorded_traffic(workload_name):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the kernel source as it is now and on this workload; else None."""
-    import hashlib
+    on the kernel sources as they are now and on this workload; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "paged_attention_decode_pa_amd", "csrc", "pa_decode.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_source_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload_name:

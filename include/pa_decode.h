@@ -27,11 +27,14 @@
  *   block_tables    [B][max_blocks]                 int32
  *   context_lens    [B]                             int32
  * dtype (PA_DTYPE_*) applies to q, k_cache, v_cache and out alike.  Scores,
- * softmax statistics and accumulation are fp32; bf16 outputs are rounded to
- * nearest even.
+ * softmax statistics and accumulation are fp32; bf16 and fp16 outputs are
+ * rounded to nearest even.  fp16 is the element type of the benchmark
+ * script's inputs (benchmark_decoding.py, setup_test_data).
  *
  * Conventions:
- *   - Supported shapes: d = 128; block_size a power of two from 16 to 256;
+ *   - Supported shapes: d in {64, 128, 256} (the benchmark script's head_dim
+ *     argument; 128 in every configuration of the docs page); block_size a
+ *     power of two from 16 to 256;
  *     H % Hkv == 0 with H / Hkv in {1, 2, 4, 8, 16}.  Others return
  *     PA_ERR_UNSUPPORTED.  Sequences are processed in tiles of 16 tokens; a
  *     row of the table covers T = max_blocks * block_size / 16 tiles.
@@ -62,7 +65,7 @@
 extern "C" {
 #endif
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_F16 = 2 } pa_dtype_t;
 
 enum {
     PA_OK = 0,

@@ -23,9 +23,10 @@ What the inputs look like follows the pages:
   flash-decoding-bench design note's KV-length sweep.
 
 Draw order for a seed (numpy ``default_rng``): q, then the K pool, then the V
-pool (all float32 standard normal), then the pool permutation.  bf16 cases
-round every float32 draw to bfloat16 with round-to-nearest-even; both the GPU
-and the oracle then see exactly those rounded values.
+pool (all float32 standard normal), then the pool permutation.  bf16 and fp16
+cases round every float32 draw to bfloat16 or IEEE half with
+round-to-nearest-even; both the GPU and the oracle then see exactly those
+rounded values.  fp16 is the element type ``setup_test_data`` draws in.
 """
 from __future__ import annotations
 
@@ -37,10 +38,13 @@ import numpy as np
 
 __all__ = [
     "Case", "CONFIGS", "make_case", "make_config_case", "bf16_round_bits",
-    "bf16_bits_to_f32", "poison_unused", "BF16_NAN_BITS",
+    "bf16_bits_to_f32", "f16_round_bits", "f16_bits_to_f32", "poison_unused",
+    "BF16_NAN_BITS", "F16_NAN_BITS", "DTYPES",
 ]
 
 BF16_NAN_BITS = 0x7FC0
+F16_NAN_BITS = 0x7E00
+DTYPES = ("f32", "bf16", "f16")
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
@@ -65,16 +69,35 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+def f16_round_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> IEEE binary16 bit patterns (uint16), round to nearest
+    even (numpy's float32 -> float16 conversion rounds that way)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):   # overflow to +-inf is the rounding rule
+        return x.astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns (uint16) -> the float32 values they encode (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return bits.view(np.float16).astype(np.float32)
+
+
+_ROUND = {"bf16": (bf16_round_bits, bf16_bits_to_f32, BF16_NAN_BITS),
+          "f16": (f16_round_bits, f16_bits_to_f32, F16_NAN_BITS)}
+
+
 @dataclasses.dataclass
 class Case:
     """One decode step's inputs, as host arrays.
 
     ``q``, ``k_cache`` and ``v_cache`` are float32 arrays holding the exact
-    values the GPU sees (for bf16 cases, values already rounded to bf16);
-    ``*_bits`` hold the bf16 bit patterns (uint16) for bf16 cases, else None.
+    values the GPU sees (for bf16 and fp16 cases, values already rounded);
+    ``*_bits`` hold the 16-bit patterns (uint16) for bf16 and fp16 cases,
+    else None.
     """
 
-    dtype: str                      # "f32" or "bf16"
+    dtype: str                      # "f32", "bf16" or "f16"
     q: np.ndarray                   # [B][H][d] float32
     k_cache: np.ndarray             # [pool][block_size][Hkv][d] float32
     v_cache: np.ndarray             # [pool][block_size][Hkv][d] float32
@@ -105,11 +128,12 @@ class Case:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return 4 if self.dtype == "f32" else 2
 
     def storage(self, which: str) -> np.ndarray:
-        """The array in its storage type: uint16 bits for bf16, float32 else."""
-        if self.dtype == "bf16":
+        """The array in its storage type: uint16 bits for bf16 and fp16,
+        float32 else."""
+        if self.dtype != "f32":
             return {"q": self.q_bits, "k": self.k_bits, "v": self.v_bits}[which]
         return {"q": self.q, "k": self.k_cache, "v": self.v_cache}[which]
 
@@ -177,8 +201,8 @@ def make_case(
     holes: (b, logical_block) pairs whose table entry is set to -1 after the
       assignment, i.e. unallocated slots inside a sequence's context.
     """
-    if dtype not in ("f32", "bf16"):
-        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
     lens = [int(ctx)] * B if np.isscalar(ctx) else [int(c) for c in ctx]
     if len(lens) != B:
         raise ValueError("one context length per sequence expected")
@@ -218,13 +242,14 @@ def make_case(
         scale=np.float32(1.0 / math.sqrt(d)), num_heads=H, num_kv_heads=Hkv,
         head_dim=d, block_size=bs, seed=seed, name=name,
     )
-    if dtype == "bf16":
-        case.q_bits = bf16_round_bits(q)
-        case.k_bits = bf16_round_bits(k)
-        case.v_bits = bf16_round_bits(v)
-        case.q = bf16_bits_to_f32(case.q_bits)
-        case.k_cache = bf16_bits_to_f32(case.k_bits)
-        case.v_cache = bf16_bits_to_f32(case.v_bits)
+    if dtype in _ROUND:
+        to_bits, to_f32, _ = _ROUND[dtype]
+        case.q_bits = to_bits(q)
+        case.k_bits = to_bits(k)
+        case.v_bits = to_bits(v)
+        case.q = to_f32(case.q_bits)
+        case.k_cache = to_f32(case.k_bits)
+        case.v_cache = to_f32(case.v_bits)
     return case
 
 
@@ -259,11 +284,12 @@ def poison_unused(case: Case) -> Case:
                 live[blk, :min(bs, n - j * bs)] = True
     out = dataclasses.replace(case, block_tables=tables)
     dead = ~live
-    if case.dtype == "bf16":
+    if case.dtype in _ROUND:
+        _, to_f32, nan_bits = _ROUND[case.dtype]
         kb = case.k_bits.copy(); vb = case.v_bits.copy()
-        kb[dead] = BF16_NAN_BITS; vb[dead] = BF16_NAN_BITS
+        kb[dead] = nan_bits; vb[dead] = nan_bits
         out.k_bits, out.v_bits = kb, vb
-        out.k_cache = bf16_bits_to_f32(kb); out.v_cache = bf16_bits_to_f32(vb)
+        out.k_cache = to_f32(kb); out.v_cache = to_f32(vb)
     else:
         k = case.k_cache.copy(); v = case.v_cache.copy()
         k[dead] = np.nan; v[dead] = np.nan

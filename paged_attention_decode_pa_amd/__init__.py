@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
+PA_DTYPE_F16 = 2
 
 PA_OK = 0
 PA_ERR_NULL = -1
@@ -110,6 +111,8 @@ def dtype_code(torch_dtype) -> int:
         return PA_DTYPE_F32
     if torch_dtype == torch.bfloat16:
         return PA_DTYPE_BF16
+    if torch_dtype == torch.float16:
+        return PA_DTYPE_F16
     raise PaError(PA_ERR_DTYPE, f"dtype {torch_dtype}")
 
 
@@ -182,6 +185,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, out=None, 
                     ("block_tables", block_tables), ("context_lens", context_lens)):
         if not t.is_contiguous():
             raise PaError(PA_ERR_SHAPE, f"{name} must be contiguous")
+        if not t.is_cuda or t.device != q.device:
+            raise PaError(PA_ERR_DEVICE, f"{name} must be on q's GPU")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise PaError(PA_ERR_DTYPE, "block_tables and context_lens must be int32")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or v_cache.shape != k_cache.shape:

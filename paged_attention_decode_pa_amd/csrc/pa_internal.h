@@ -1,0 +1,91 @@
+// pa_internal.h -- what the host launcher (pa_decode.hip) and the kernel
+// translation units (pa_kernels_*.hip) share: the kernel parameter blocks,
+// the launch constants, the table of built shapes and the launcher entry
+// points, one instantiation per element type.
+#ifndef PA_INTERNAL_H
+#define PA_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa_decode.h"
+
+namespace pa_detail {
+
+constexpr int kWave = 64;
+// The kernels walk a sequence in tiles of 16 tokens, the row count of one MFMA
+// tile.  A physical block of block_size tokens (a power of two from 16 to 256)
+// holds block_size / 16 tiles; each tile lies inside one block.
+constexpr int kTile = 16;
+constexpr int kMaxBlockSize = 256;
+
+#ifndef PA_WAVES_PER_GROUP
+#define PA_WAVES_PER_GROUP 4
+#endif
+constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;  // waves per workgroup
+
+// What a workgroup does with its merged (M, L, O).
+enum Mode { kSingle = 0, kPartials = 1, kFused = 2 };
+
+struct Params {
+    const char *q;
+    const char *k;
+    const char *v;
+    const int32_t *table;
+    const int32_t *lens;
+    void *out;          // [B][H][d] dtype (single pass, fused merge)
+    float2 *part_ml;    // [B][H][P] (max, sum)
+    float *part_acc;    // [B][H][P][d]
+    int *counters;      // [B][Hkv] arrival tickets (fused mode), zero between calls
+    long long blk_bytes;  // bytes per physical block: block_size * Hkv * d * esize
+    long long pool;       // > 0: ids >= pool are skipped
+    int tok_bytes;        // bytes between tokens of a block: Hkv * d * esize
+    int B, H, Hkv, max_blocks, P;
+    int tiles_log2;       // log2(block_size / 16): tiles per physical block
+    int max_tiles;        // max_blocks * block_size / 16
+    int bpp;              // tiles per partition
+    float qk_scale;       // scale * log2(e)
+};
+
+struct MergeParams {
+    const float2 *part_ml;
+    const float *part_acc;
+    void *out;
+    int B, H, P, d;
+};
+
+// The (dtype, head dim, group size) combinations with a kernel.  One
+// workgroup keeps the fp32 accumulators of all G heads of its group in
+// registers (G * d / 16 per lane) next to the tiles in flight; the
+// combinations left out would not fit the register file without spilling to
+// scratch memory.
+constexpr bool shape_built(int dtype, int d, int G) {
+    if (d != 64 && d != 128 && d != 256) return false;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
+    if (d == 256) return dtype == PA_DTYPE_F32 ? G <= 2 : G <= 8;
+    return true;
+}
+
+// Launch the decode kernel for element type DT on `groups` workgroups of
+// kWavesPerGroup waves (shape_built(DT, d, G) must hold), or the merge kernel
+// on one wave per (b, h).  Return the launch's hipGetLastError().
+template <int DT>
+hipError_t launch_decode(const Params &p, int d, int G, int mode, int groups,
+                         hipStream_t stream);
+template <int DT>
+hipError_t launch_merge(const MergeParams &mp, int groups, hipStream_t stream);
+
+extern template hipError_t launch_decode<PA_DTYPE_F32>(const Params &, int, int, int, int,
+                                                       hipStream_t);
+extern template hipError_t launch_decode<PA_DTYPE_BF16>(const Params &, int, int, int, int,
+                                                        hipStream_t);
+extern template hipError_t launch_decode<PA_DTYPE_F16>(const Params &, int, int, int, int,
+                                                       hipStream_t);
+extern template hipError_t launch_merge<PA_DTYPE_F32>(const MergeParams &, int, hipStream_t);
+extern template hipError_t launch_merge<PA_DTYPE_BF16>(const MergeParams &, int, hipStream_t);
+extern template hipError_t launch_merge<PA_DTYPE_F16>(const MergeParams &, int, hipStream_t);
+
+}  // namespace pa_detail
+
+#endif  // PA_INTERNAL_H

@@ -1,0 +1,615 @@
+// pa_kernels.h -- the decode and merge kernels for gfx950, as templates over
+// the element type DT, head dim D and group size G, and the launchers that
+// pick an instance.  Each pa_kernels_<dtype>.hip instantiates the launchers
+// for one element type, so the three compile in parallel.
+//
+// Design (one work unit = one (sequence b, kv head kvh) pair, optionally one
+// partition of its context):
+//
+// * One workgroup per (kvh, b[, partition]) serves all G = H / Hkv query heads
+//   of the group, so each K/V row is read from HBM once per kv head, not once
+//   per query head.
+// * A wave consumes one 16-token tile per step.  Block ids are read with
+//   scalar loads one group of tiles ahead, so they are wave-uniform and each
+//   tile gets a raw buffer descriptor (SGPRs) over exactly its live rows of
+//   head kvh; the per-lane offsets never change.  Slots past the context and
+//   -1 blocks fall outside the descriptor's range and read as zeros without a
+//   memory access, so the streaming loop has no branches.
+// * Scores: the 16 tokens x G heads x D product is a small dense contraction,
+//   run on the matrix cores: rows = the tile's 16 tokens, columns = the G
+//   query heads repeated to 16, reduction = head_dim.  Each lane's 16-byte K
+//   load is exactly its MFMA A operand, so no cross-lane reduction is needed
+//   for q.K.  After the MFMAs lane (row g = lane/16, column c = lane%16) holds
+//   the scores of tokens 4g..4g+3 for head c % G.
+// * Online softmax per (row g, head): running max m and normaliser l in log2
+//   units (scale * log2 e is folded into one multiply), so each lane updates
+//   its own statistics from its 4 scores with no cross-lane max per tile.
+// * V accumulate on the vector ALUs in fp32: lane (g, c) holds D / 16 elements
+//   of the V rows of tokens 4g..4g+3 and accumulates them for all G heads; the
+//   weights of the other heads come from neighbouring lanes by DPP broadcast.
+// * Epilogue: the 4 row groups of a wave are merged with permlane swaps, the
+//   waves through LDS, always with the rescale-and-sum rule
+//   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)).  A single
+//   pass writes O / L.  With partitions, each workgroup writes (M, L, O) to
+//   the workspace; then either a separate merge kernel combines them, or (fused
+//   mode) the last workgroup of each (b, kvh) to finish -- found with an atomic
+//   ticket -- combines them with the same rule and writes out.
+#ifndef PA_KERNELS_H
+#define PA_KERNELS_H
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <utility>
+
+#include "pa_internal.h"
+
+namespace pa_detail {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+// Start value of a running max: finite, so 2^(m - m') never sees inf - inf.
+constexpr float kMaxInit = -1.0e30f;
+
+#ifndef PA_PIPELINE_DEPTH
+#define PA_PIPELINE_DEPTH 2
+#endif
+constexpr int kDepth = PA_PIPELINE_DEPTH;           // tiles in flight per wave
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on GFX9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT> struct ElemBytes;
+template <> struct ElemBytes<PA_DTYPE_F32> { static constexpr int value = 4; };
+template <> struct ElemBytes<PA_DTYPE_BF16> { static constexpr int value = 2; };
+template <> struct ElemBytes<PA_DTYPE_F16> { static constexpr int value = 2; };
+
+// Load geometry of one 16-token tile for element type DT and head dim D.
+// Lane (g = lane / 16, c16 = lane % 16):
+//  * K: token c16's 16-byte chunks 4m + g, m < kKLoads -- exactly the MFMA A
+//    operand of reduction step m (the query's B operand uses the same chunks);
+//  * V: kVElems = D / 16 elements of each of tokens 4g..4g+3, read as kVLoads
+//    loads of kVWidth bytes; load s of token r starts at byte
+//    16 * kVWidth * s + kVWidth * c16 of the row, so the 16 lanes of a row
+//    read each 16 * kVWidth-byte stretch of the row together.
+template <int DT, int D>
+struct Geometry {
+    static constexpr int kEs = ElemBytes<DT>::value;
+    static constexpr int kRowBytes = D * kEs;
+    static constexpr int kKLoads = kRowBytes / 64;
+    static constexpr int kVElems = D / 16;
+    static constexpr int kVWidth = kVElems * kEs < 16 ? kVElems * kEs : 16;
+    static constexpr int kVLoads = kVElems * kEs / kVWidth;
+    static constexpr int kVWords = kVElems * kEs / 4;   // 32-bit words per token
+    static constexpr int kElemsPerLoad = kVWidth / kEs;
+    static_assert(kKLoads >= 1 && kRowBytes % 64 == 0, "head dim too small for the K layout");
+    static_assert(kVWidth == 8 || kVWidth == 16, "V loads are 8 or 16 bytes");
+};
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value of x held by the lane of this lane's group of G lanes that serves head H_.
+template <int G, int H_>
+__device__ __forceinline__ float group_bcast(float x) {
+    if constexpr (G == 1) {
+        return x;
+    } else if constexpr (G == 2) {
+        constexpr int ctrl = H_ | (H_ << 2) | ((2 + H_) << 4) | ((2 + H_) << 6);
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+    } else if constexpr (G == 4) {
+        constexpr int ctrl = H_ * 0x55;  // quad_perm [H_, H_, H_, H_]
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+    } else {
+        // ds_swizzle bit-mask mode: lane' = (lane & and_mask) | or_mask within 32 lanes
+        constexpr int and_mask = G == 8 ? 0x18 : 0x10;
+        constexpr int pattern = and_mask | (H_ << 5);
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), pattern));
+    }
+}
+
+// x combined over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48), result in
+// every lane: a swap of the two 32-lane halves, then of neighbouring rows.
+template <typename Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(y);
+    const auto c = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    return across_rows(x, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float rows_max(float x) {
+    return across_rows(x, [](float a, float b) { return fmaxf(a, b); });
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Word i of a row chunk -> its elements as fp32 (two for 16-bit types).
+template <int DT>
+__device__ __forceinline__ void unpack_word(unsigned w, float *f) {
+    if constexpr (DT == PA_DTYPE_BF16) {
+        f[0] = __uint_as_float(w << 16);
+        f[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else if constexpr (DT == PA_DTYPE_F16) {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        f[0] = static_cast<float>(h[0]);
+        f[1] = static_cast<float>(h[1]);
+    } else {
+        f[0] = __uint_as_float(w);
+    }
+}
+
+template <int G, int VE>
+struct WaveState {
+    float m;            // running max (log2 units) of this lane's (row, head)
+    float l;            // running normaliser
+    float acc[G][VE];   // unnormalised sum of p * V for every head of the group
+};
+
+// One tile's scores, softmax update and V accumulation.  nlive = tokens of the
+// tile that take part (0..16); K/V slots at or past nlive were read as zeros
+// (they lie outside the tile's buffer range), so only their scores need
+// masking.
+template <int DT, int D, int G>
+__device__ __forceinline__ void consume_tile(WaveState<G, D / 16> &st, const u32x4 *kr,
+                                             const unsigned (*vw)[Geometry<DT, D>::kVWords],
+                                             const u32x4 *qr, float qk_scale, int g, int nlive) {
+    using Geo = Geometry<DT, D>;
+    constexpr int VE = Geo::kVElems;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == PA_DTYPE_BF16) {
+#pragma unroll
+        for (int m = 0; m < Geo::kKLoads; ++m)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[m]),
+                                                         __builtin_bit_cast(bf16x8, qr[m]), c,
+                                                         0, 0, 0);
+    } else if constexpr (DT == PA_DTYPE_F16) {
+#pragma unroll
+        for (int m = 0; m < Geo::kKLoads; ++m)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[m]),
+                                                        __builtin_bit_cast(f16x8, qr[m]), c,
+                                                        0, 0, 0);
+    } else {
+#pragma unroll
+        for (int m = 0; m < Geo::kKLoads; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr[m][j]),
+                                                          __uint_as_float(qr[m][j]), c, 0, 0, 0);
+    }
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = (4 * g + r < nlive) ? c[r] * qk_scale : -INFINITY;
+    const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    const float mn = fmaxf(st.m, bm);
+    const float alpha = fast_exp2(st.m - mn);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - mn);
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    st.m = mn;
+
+    static_for<G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float a = group_bcast<G, h>(alpha);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) st.acc[h][e] *= a;
+    });
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float vf[VE];
+        constexpr int per_word = 4 / Geo::kEs;
+#pragma unroll
+        for (int i = 0; i < Geo::kVWords; ++i) unpack_word<DT>(vw[r][i], vf + per_word * i);
+        static_for<G>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const float ph = group_bcast<G, h>(p[r]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) st.acc[h][e] = fmaf(ph, vf[e], st.acc[h][e]);
+        });
+    }
+}
+
+// Head-dim element held in accumulator slot e by the lane in column c16.
+template <int DT, int D>
+__device__ __forceinline__ int acc_elem(int c16, int e) {
+    constexpr int epl = Geometry<DT, D>::kElemsPerLoad;
+    return (e / epl) * 16 * epl + epl * c16 + e % epl;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_pair(void *out, long long idx, float x0, float x1) {
+    if constexpr (DT == PA_DTYPE_BF16) {
+        const bf16x2 v = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+        *reinterpret_cast<bf16x2 *>(static_cast<__bf16 *>(out) + idx) = v;
+    } else if constexpr (DT == PA_DTYPE_F16) {
+        const f16x2 v = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+        *reinterpret_cast<f16x2 *>(static_cast<_Float16 *>(out) + idx) = v;
+    } else {
+        *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) = make_float2(x0, x1);
+    }
+}
+
+// Raw buffer descriptor over [base, base + nbytes): loads at offsets >= nbytes
+// return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char *base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, nbytes, kRsrcWord3);
+}
+
+#ifndef PA_KV_CACHE_POLICY
+#define PA_KV_CACHE_POLICY 2
+#endif
+// Cache-policy bits of the K/V stream loads (the buffer instruction's aux field):
+// 2 = non-temporal, so the single-use stream does not evict the table, the
+// query, the partials or the kernel code from the caches.
+constexpr int kKvPolicy = PA_KV_CACHE_POLICY;
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kKvPolicy));
+}
+
+// BYTES (8 or 16) bytes at `off` into dst[0 .. BYTES / 4).
+template <int BYTES>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, unsigned off, unsigned *dst) {
+    if constexpr (BYTES == 16) {
+        const u32x4 x = load16(r, off);
+        dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+    } else {
+        const u32x2 x = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kKvPolicy));
+        dst[0] = x[0]; dst[1] = x[1];
+    }
+}
+
+// Float pair access at agent scope.  The split kernel's fused merge exchanges
+// partials between workgroups that may run on different XCDs (each with its own
+// L2): these stores write through to the device-coherent level and these loads
+// read from it, so no L2 writeback or invalidate is needed.
+__device__ __forceinline__ void store_pair_coherent(float *p, float x0, float x1) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
+                       __builtin_bit_cast(unsigned long long, make_float2(x0, x1)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_pair_coherent(const float *p) {
+    return __builtin_bit_cast(
+        float2, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_pair(const float *p) {
+    if constexpr (COHERENT) return load_pair_coherent(p);
+    else return *reinterpret_cast<const float2 *>(p);
+}
+
+// Combine the P partitions of (b, h) for head-dim elements e, e + 1 with the
+// rescale-and-sum rule, running over the partitions in order.  ml points at
+// the (max, sum) pairs of (b, h), acc at element e of its first partition;
+// partitions are d floats apart.  Returns the normalised pair (zeros when no
+// partition saw a live token).  All loads of a chunk of CHUNK partitions leave
+// before the first is used.  Reads past P are clamped to the last partition
+// and replaced by an empty partition (max -1e30, sum 0, zeros), which leaves
+// the running state as it is.
+template <int CHUNK, bool COHERENT>
+__device__ __forceinline__ float2 merge_chunked(const float2 *ml, const float *acc, int P, int d) {
+    float M = kMaxInit, L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int q0 = 0; q0 < P; q0 += CHUNK) {
+        float2 s[CHUNK], a[CHUNK];
+#pragma unroll
+        for (int j = 0; j < CHUNK; ++j) {
+            const int q = q0 + j < P ? q0 + j : P - 1;
+            s[j] = load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q));
+            a[j] = load_pair<COHERENT>(acc + (long long)q * d);
+        }
+#pragma unroll
+        for (int j = 0; j < CHUNK; ++j) {
+            const bool live = q0 + j < P;
+            s[j] = live ? s[j] : make_float2(kMaxInit, 0.f);
+            a[j] = live ? a[j] : make_float2(0.f, 0.f);
+            const float mn = fmaxf(M, s[j].x);
+            const float fo = fast_exp2(M - mn), fp = fast_exp2(s[j].x - mn);
+            L = L * fo + s[j].y * fp;
+            o0 = o0 * fo + a[j].x * fp;
+            o1 = o1 * fo + a[j].y * fp;
+            M = mn;
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    return make_float2(o0 * inv, o1 * inv);
+}
+
+// The chunk is the smallest of 4, 8, 16, 32 that holds P (32 beyond that), so
+// few partitions do not pay for loads of padding.
+template <bool COHERENT>
+__device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float *acc, int P,
+                                                   int d) {
+    if (P <= 4) return merge_chunked<4, COHERENT>(ml, acc, P, d);
+    if (P <= 8) return merge_chunked<8, COHERENT>(ml, acc, P, d);
+    if (P <= 16) return merge_chunked<16, COHERENT>(ml, acc, P, d);
+    return merge_chunked<32, COHERENT>(ml, acc, P, d);
+}
+
+template <int DT, int D, int G, int NW, int DEPTH, int MODE>
+__global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
+    using Geo = Geometry<DT, D>;
+    constexpr int KL = Geo::kKLoads, VE = Geo::kVElems, VW = Geo::kVWords;
+    constexpr int VLD = Geo::kVLoads, VWIDTH = Geo::kVWidth;
+
+    const int wg = blockIdx.x;
+    const int kvh = wg % p.Hkv;
+    const int b = (wg / p.Hkv) % p.B;
+    const int part = wg / (p.Hkv * p.B);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
+    const int lane = threadIdx.x % kWave;
+    const int c16 = lane & 15;  // MFMA column / token of the tile for K
+    const int g = lane >> 4;    // MFMA row group: tokens 4g..4g+3 for V
+
+    const int lo = part * p.bpp;
+    const int first = lo + wave;  // this wave's tiles: first, first + NW, ...
+    const int32_t *trow = p.table + (long long)b * p.max_blocks;
+    // Table entry of the block holding the wave's i-th tile, the read clamped
+    // into the row so it always stays in bounds (entries past the context are
+    // read, never used).
+    auto tile_of = [&](int i) -> int { return first + NW * i; };
+    auto table_at = [&](int i) -> int {
+        const int e = tile_of(i) >> p.tiles_log2;
+        return trow[e < p.max_blocks ? e : p.max_blocks - 1];
+    };
+
+    // Independent loads first: the context length, the first group's table
+    // entries and the query all leave before any of them is waited for.
+    int ctx = p.lens[b];
+    int raw0[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) raw0[s] = table_at(s);
+    // B operand: the query of head kvh*G + c16%G, chunk (4m + g) of 16 bytes.
+    const char *qrow = p.q + ((long long)b * p.H + kvh * G + (c16 % G)) * Geo::kRowBytes;
+    u32x4 qr[KL];
+#pragma unroll
+    for (int m = 0; m < KL; ++m) qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
+
+    ctx = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
+    const int ntiles = (ctx + kTile - 1) / kTile;
+    const int hi = min(lo + p.bpp, ntiles);
+    const int nw = hi > first ? (hi - first + NW - 1) / NW : 0;
+
+    // Per-lane byte offsets inside one tile's rows of head kvh; never change.
+    const unsigned koff = c16 * p.tok_bytes + 16 * g;
+    unsigned voff[4][VLD];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < VLD; ++s)
+            voff[r][s] = (4 * g + r) * p.tok_bytes + VWIDTH * c16 + 16 * VWIDTH * s;
+    const char *kbase = p.k + kvh * Geo::kRowBytes;
+    const char *vbase = p.v + kvh * Geo::kRowBytes;
+
+    WaveState<G, VE> st;
+    st.m = kMaxInit;
+    st.l = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) st.acc[h][e] = 0.f;
+
+    // Live tokens of the wave's i-th tile given its block's table entry: 0 past
+    // the wave's range and for -1 (or out-of-pool) entries.
+    auto live_tokens = [&](int i, int id) -> int {
+        const int j = tile_of(i);
+        if (j >= hi || id < 0 || (p.pool > 0 && id >= p.pool)) return 0;
+        const int rem = ctx - j * kTile;
+        return rem < kTile ? rem : kTile;
+    };
+    // Loads of the wave's i-th tile: its rows start at the block's base plus
+    // the tile's place inside the block.
+    auto issue = [&](u32x4 *kd, unsigned (*vd)[VW], int i, int id, int nlive) {
+        const int in_block = tile_of(i) & ((1 << p.tiles_log2) - 1);
+        const long long off =
+            nlive > 0 ? (long long)id * p.blk_bytes + (long long)in_block * kTile * p.tok_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off, nlive * p.tok_bytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off, nlive * p.tok_bytes);
+#pragma unroll
+        for (int m = 0; m < KL; ++m) kd[m] = load16(rk, koff + 64 * m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int s = 0; s < VLD; ++s)
+                load_words<VWIDTH>(rv, voff[r][s], vd[r] + s * (VWIDTH / 4));
+    };
+
+    if (nw > 0) {
+        // DEPTH tiles in flight: slot s of group k holds the wave's tile kDEPTH + s.
+        u32x4 kr[DEPTH][KL];
+        unsigned vr[DEPTH][4][VW];
+        int nl[DEPTH];
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+            nl[s] = live_tokens(s, raw0[s]);
+            issue(kr[s], vr[s], s, raw0[s], nl[s]);
+        }
+        const int ngroups = (nw + DEPTH - 1) / DEPTH;
+        for (int k = 0; k < ngroups; ++k) {
+            int nid[DEPTH];
+#pragma unroll
+            for (int s = 0; s < DEPTH; ++s) nid[s] = table_at((k + 1) * DEPTH + s);
+#pragma unroll
+            for (int s = 0; s < DEPTH; ++s) {
+                consume_tile<DT, D, G>(st, kr[s], vr[s], qr, p.qk_scale, g, nl[s]);
+                nl[s] = live_tokens((k + 1) * DEPTH + s, nid[s]);
+                issue(kr[s], vr[s], (k + 1) * DEPTH + s, nid[s], nl[s]);
+            }
+        }
+    }
+
+    // ---- merge the 4 row groups of the wave -----------------------------------
+    // The (m, l) of row g and head h sit in the lanes of row g whose column is
+    // h modulo G; after the merge every row holds the same totals.
+    float mh[G], lh[G];
+    static_for<G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        mh[h] = group_bcast<G, h>(st.m);
+        lh[h] = group_bcast<G, h>(st.l);
+    });
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float M = rows_max(mh[h]);
+        const float f = fast_exp2(mh[h] - M);
+        lh[h] = rows_sum(lh[h] * f);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) st.acc[h][e] = rows_sum(st.acc[h][e] * f);
+        mh[h] = M;
+    }
+
+    // ---- merge the waves through LDS ------------------------------------------
+    __shared__ float2 sm_ml[NW][G];
+    __shared__ float sm_acc[NW][G][D];
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) sm_acc[wave][h][acc_elem<DT, D>(c16, e)] = st.acc[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sm_ml[wave][h] = make_float2(mh[h], lh[h]);
+    }
+    __syncthreads();
+
+    // Thread t handles head h = idx / (D / 2) and elements 2 (idx % (D / 2)) + {0, 1}.
+    for (int idx = threadIdx.x; idx < G * (D / 2); idx += NW * kWave) {
+        const int h = idx / (D / 2), e = 2 * (idx % (D / 2));
+        float M = kMaxInit;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][h].x);
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(sm_ml[w][h].x - M);
+            L = fmaf(sm_ml[w][h].y, f, L);
+            o0 = fmaf(sm_acc[w][h][e], f, o0);
+            o1 = fmaf(sm_acc[w][h][e + 1], f, o1);
+        }
+        const long long bh = (long long)b * p.H + kvh * G + h;
+        if constexpr (MODE == kSingle) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            store_pair<DT>(p.out, bh * D + e, o0 * inv, o1 * inv);
+        } else if constexpr (MODE == kPartials) {
+            *reinterpret_cast<float2 *>(p.part_acc + (bh * p.P + part) * D + e) =
+                make_float2(o0, o1);
+            if (e == 0) p.part_ml[bh * p.P + part] = make_float2(M, L);
+        } else {
+            store_pair_coherent(p.part_acc + (bh * p.P + part) * D + e, o0, o1);
+            if (e == 0)
+                store_pair_coherent(reinterpret_cast<float *>(p.part_ml + bh * p.P + part), M, L);
+        }
+    }
+
+    if constexpr (MODE == kFused) {
+        // Publish this partition (its coherent stores complete before the
+        // barrier), take a ticket; the last of the P workgroups of (b, kvh)
+        // merges all partitions and resets the ticket for the next call.
+        __shared__ int sm_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int prev = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == p.P - 1;
+        }
+        __syncthreads();
+        if (sm_last) {
+            for (int idx = threadIdx.x; idx < G * (D / 2); idx += NW * kWave) {
+                const int h = idx / (D / 2), e = 2 * (idx % (D / 2));
+                const long long bh = (long long)b * p.H + kvh * G + h;
+                const float2 o = merge_partitions<true>(p.part_ml + bh * p.P,
+                                                        p.part_acc + bh * p.P * D + e, p.P, D);
+                store_pair<DT>(p.out, bh * D + e, o.x, o.y);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(p.counters + b * p.Hkv + kvh, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+
+// One wave per (b, h); lane l produces elements 2l + 128 j, 2l + 1 + 128 j.
+template <int DT>
+__global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
+    const long long bh = blockIdx.x;
+    for (int e = 2 * threadIdx.x; e < mp.d; e += 2 * kWave) {
+        const float2 o = merge_partitions<false>(mp.part_ml + bh * mp.P,
+                                                 mp.part_acc + bh * mp.P * mp.d + e, mp.P, mp.d);
+        store_pair<DT>(mp.out, bh * mp.d + e, o.x, o.y);
+    }
+}
+
+template <int DT, int D, int G, int MODE>
+hipError_t launch_instance(const Params &p, int groups, hipStream_t stream) {
+    if constexpr (shape_built(DT, D, G)) {
+        hipLaunchKernelGGL((pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
+                           dim3(groups), dim3(kWavesPerGroup * kWave), 0, stream, p);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int D, int MODE>
+hipError_t dispatch_g(const Params &p, int G, int groups, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_instance<DT, D, 1, MODE>(p, groups, stream);
+        case 2: return launch_instance<DT, D, 2, MODE>(p, groups, stream);
+        case 4: return launch_instance<DT, D, 4, MODE>(p, groups, stream);
+        case 8: return launch_instance<DT, D, 8, MODE>(p, groups, stream);
+        case 16: return launch_instance<DT, D, 16, MODE>(p, groups, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int D>
+hipError_t dispatch_mode(const Params &p, int G, int mode, int groups, hipStream_t stream) {
+    switch (mode) {
+        case kSingle: return dispatch_g<DT, D, kSingle>(p, G, groups, stream);
+        case kPartials: return dispatch_g<DT, D, kPartials>(p, G, groups, stream);
+        default: return dispatch_g<DT, D, kFused>(p, G, groups, stream);
+    }
+}
+
+template <int DT>
+hipError_t launch_decode(const Params &p, int d, int G, int mode, int groups,
+                         hipStream_t stream) {
+    switch (d) {
+        case 64: return dispatch_mode<DT, 64>(p, G, mode, groups, stream);
+        case 128: return dispatch_mode<DT, 128>(p, G, mode, groups, stream);
+        case 256: return dispatch_mode<DT, 256>(p, G, mode, groups, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT>
+hipError_t launch_merge(const MergeParams &mp, int groups, hipStream_t stream) {
+    hipLaunchKernelGGL(pa_merge_kernel<DT>, dim3(groups), dim3(kWave), 0, stream, mp);
+    return hipGetLastError();
+}
+
+}  // namespace pa_detail
+
+#endif  // PA_KERNELS_H

@@ -92,8 +92,11 @@ def call(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=64), pa.PA_ERR_UNSUPPORTED),
-    (dict(d=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=256, H=128, Hkv=8), pa.PA_ERR_UNSUPPORTED),          # G = 16 at d = 256
+    (dict(d=256, H=32, Hkv=8, dtype=0), pa.PA_ERR_UNSUPPORTED),  # fp32, G = 4 at d = 256
+    (dict(Hkv=1 << 20, H=1 << 20), pa.PA_ERR_UNSUPPORTED),      # tile offsets past 2^31
     (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=48), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=512), pa.PA_ERR_UNSUPPORTED),
@@ -102,7 +105,7 @@ def call(**kw):
     (dict(B=-1), pa.PA_ERR_SHAPE),
     (dict(H=0), pa.PA_ERR_SHAPE),
     (dict(mb=0), pa.PA_ERR_SHAPE),
-    (dict(dtype=2), pa.PA_ERR_DTYPE),
+    (dict(dtype=3), pa.PA_ERR_DTYPE),
     (dict(dtype=-1), pa.PA_ERR_DTYPE),
     (dict(scale=float("nan")), pa.PA_ERR_VALUE),
     (dict(scale=float("inf")), pa.PA_ERR_VALUE),
@@ -131,6 +134,12 @@ def test_valid_call_without_device_reports_device_error():
     assert call() == pa.PA_ERR_DEVICE
     for bs in (16, 32, 64, 128, 256):  # every supported block size passes validation
         assert call(bs=bs) == pa.PA_ERR_DEVICE
+    for dtype in (0, 1, 2):
+        for d in (64, 128, 256):
+            for H in (8, 16, 32, 64, 128):
+                built = d < 256 or H // 8 <= (2 if dtype == 0 else 8)
+                want = pa.PA_ERR_DEVICE if built else pa.PA_ERR_UNSUPPORTED
+                assert call(dtype=dtype, d=d, H=H, Hkv=8) == want, (dtype, d, H)
 
 
 def test_ex_and_split_half_validation():
@@ -152,7 +161,7 @@ def test_ex_and_split_half_validation():
         pa.PA_ERR_WORKSPACE
     assert lib.pa_merge_partials(FAKE["out"], 0x700000, need - 1, 1, 32, 128, 4, 1, None) == \
         pa.PA_ERR_WORKSPACE
-    assert lib.pa_merge_partials(FAKE["out"], 0x700000, need, 1, 32, 64, 4, 1, None) == \
+    assert lib.pa_merge_partials(FAKE["out"], 0x700000, need, 1, 32, 96, 4, 1, None) == \
         pa.PA_ERR_UNSUPPORTED
     assert lib.pa_merge_partials(0x700000 + 64, 0x700000, need, 1, 32, 128, 4, 1, None) == \
         pa.PA_ERR_ALIAS
@@ -167,7 +176,10 @@ def test_binding_rejects_bad_tensors():
     k = torch.zeros(4, 16, 8, 128, dtype=torch.float16)
     t = torch.zeros(2, 2, dtype=torch.int32)
     n = torch.zeros(2, dtype=torch.int32)
-    with pytest.raises(pa.PaError):
+    with pytest.raises(pa.PaError):   # host tensors are never handed to the library
         pa.decode(q, k, k, t, n, 0.1)
     with pytest.raises(pa.PaError):
         pa.decode(q.float(), k.float(), k.float(), t.long(), n, 0.1)
+    with pytest.raises(pa.PaError):
+        pa.dtype_code(torch.float64)
+    assert pa.dtype_code(torch.float16) == pa.PA_DTYPE_F16

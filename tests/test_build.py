@@ -1,7 +1,6 @@
 """The HIP library builds for gfx950 with no kernel using scratch memory (a
 spilled or dynamically indexed register array would silently cost a memory
 round trip per access)."""
-import os
 import re
 import subprocess
 import tempfile
@@ -11,13 +10,19 @@ from paged_attention_decode_pa_amd import build as hip_build
 
 def test_no_kernel_uses_scratch():
     with tempfile.TemporaryDirectory() as tmp:
-        cmd = [hip_build.HIPCC, *hip_build.FLAGS, "-I", os.path.join(hip_build.ROOT, "include"),
-               "-Rpass-analysis=kernel-resource-usage", hip_build.SRC,
-               "-o", os.path.join(tmp, "lib.so")]
-        res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-2000:]
-    names = re.findall(r"Function Name: (\S+)", res.stderr)
-    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", res.stderr)]
-    assert len(names) >= 32 and len(scratch) == len(names)
+        results = hip_build.compile_objects(hip_build.KERNEL_SOURCES, tmp,
+                                            extra=["-Rpass-analysis=kernel-resource-usage"])
+    names, scratch = [], []
+    for src, _, rc, err in results:
+        assert rc == 0, err[-2000:]
+        n = re.findall(r"Function Name: (\S+)", err)
+        s = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", err)]
+        assert len(n) == len(s) and n, src
+        names += n
+        scratch += s
+    # built (d, G) pairs: fp32 5 + 5 + 2, bf16 and fp16 5 + 5 + 4; 3 modes each
+    decode = [n for n in names if "pa_decode_kernel" in n]
+    assert len(decode) == (12 + 14 + 14) * 3
+    assert sum("pa_merge_kernel" in n for n in names) == 3
     bad = [n for n, s in zip(names, scratch) if s != 0]
     assert not bad, f"kernels using scratch: {bad}"

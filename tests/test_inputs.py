@@ -1,4 +1,5 @@
-"""The seeded generator: determinism, bf16 rounding, table structure, poisoning."""
+"""The seeded generator: determinism, bf16 and fp16 rounding, table structure,
+poisoning."""
 import math
 
 import numpy as np
@@ -32,6 +33,38 @@ def test_bf16_rounding_matches_torch():
     back = pi.bf16_bits_to_f32(ours)
     ref_back = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
     assert np.array_equal(back.view(np.uint32), ref_back.view(np.uint32))
+
+
+def test_f16_rounding_is_nearest_even():
+    # IEEE binary16 keeps 10 fraction bits: the spacing just above 1 is 2^-10.
+    # 1 + 2^-11 lies halfway between 1 and 1 + 2^-10 and goes to the even 1;
+    # 1 + 3 * 2^-11 lies halfway between 1 + 2^-10 and 1 + 2^-9 and goes to the
+    # even 1 + 2^-9; just above a halfway point goes up.
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -20,
+                  65504.0, 65520.0, 2.0 ** -24, 2.0 ** -26], dtype=np.float32)
+    bits = pi.f16_round_bits(x)
+    assert bits.tolist() == [0x3C00, 0x3C02, 0x3C01, 0x7BFF, 0x7C00, 0x0001, 0x0000]
+    rng = np.random.default_rng(0)
+    y = rng.standard_normal(100000).astype(np.float32) * 10
+    ours = pi.f16_round_bits(y)
+    ref = torch.from_numpy(y).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = pi.f16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(y).to(torch.float16).float().numpy())
+    # the rounded value is a nearest binary16 neighbour: within half a spacing
+    spacing = np.spacing(np.abs(back).astype(np.float16)).astype(np.float32)
+    assert (np.abs(back - y) <= spacing / 2).all()
+
+
+def test_f16_case_holds_rounded_values():
+    case = pi.make_case(2, [20, 5], 4, 2, 8, 16, dtype="f16", seed=3, pool=4)
+    assert case.elem_bytes == 2 and case.storage("k") is case.k_bits
+    assert np.array_equal(case.k_cache, pi.f16_bits_to_f32(case.k_bits))
+    ref = pi.make_case(2, [20, 5], 4, 2, 8, 16, dtype="f32", seed=3, pool=4)
+    assert np.array_equal(case.k_bits, pi.f16_round_bits(ref.k_cache))
+    assert np.array_equal(case.block_tables, ref.block_tables)
+    p = pi.poison_unused(case)
+    assert (p.k_bits == pi.F16_NAN_BITS).any() and np.isnan(p.k_cache).any()
 
 
 def test_nan_rounds_to_nan():
@@ -112,4 +145,4 @@ def test_bad_arguments():
     with pytest.raises(ValueError):
         pi.make_case(2, 32, 4, 2, 8, 16, pool=3)
     with pytest.raises(ValueError):
-        pi.make_case(1, 16, 4, 2, 8, 16, dtype="f16")
+        pi.make_case(1, 16, 4, 2, 8, 16, dtype="f64")

@@ -2,8 +2,8 @@
 
 Covers the five named workloads at full size (heuristic partition count, the
 configuration the benchmark times), forced partition counts, ragged and
-empty contexts, -1 holes, every supported group size, both dtypes, and the
-invariants that must hold bitwise on the GPU too (block permutation, NaN in
+empty contexts, -1 holes, every built group size, head dim and block size,
+the three dtypes, and the invariants that must hold bitwise on the GPU too (block permutation, NaN in
 unused slots, context length 1, repeatability, split halves == fused call).
 """
 import math
@@ -53,7 +53,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape", RAGGED)
 @pytest.mark.parametrize("parts", [0, 1, 3, 16])
 def test_ragged_lengths_holes_and_groups(gpu, dtype, shape, parts):
@@ -72,7 +72,7 @@ def test_ragged_lengths_holes_and_groups(gpu, dtype, shape, parts):
             assert (out[b].float() == 0).all()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_block_permutation_is_bitwise_invariant(gpu, dtype):
     case = pi.make_case(3, [200, 47, 16], 32, 8, 128, 16, dtype=dtype, seed=5, pool=20)
     perm = np.random.default_rng(3).permutation(20).astype(np.int32)
@@ -93,7 +93,7 @@ def test_block_permutation_is_bitwise_invariant(gpu, dtype):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_context_len_one_returns_v_row_bitwise(gpu, dtype):
     case = pi.make_case(4, [1, 1, 1, 1], 32, 8, 128, 16, dtype=dtype, seed=6, max_blocks=40,
                         pool=12)
@@ -103,14 +103,14 @@ def test_context_len_one_returns_v_row_bitwise(gpu, dtype):
         for b in range(4):
             blk = case.block_tables[b, 0]
             for h in range(32):
-                if dtype == "bf16":
+                if dtype != "f32":
                     row = torch.from_numpy(case.v_bits[blk, 0, h // 4].view(np.int16))
                     assert torch.equal(out[b, h].view(torch.int16), row)
                 else:
                     assert torch.equal(out[b, h], torch.from_numpy(case.v_cache[blk, 0, h // 4]))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_nan_in_unused_slots_never_leaks(gpu, dtype):
     case = pi.make_case(4, [37, 16, 3, 250], 32, 8, 128, 16, dtype=dtype, seed=7,
                         max_blocks=20, pool=30)
@@ -311,13 +311,79 @@ def test_block_sizes(gpu, dtype, shape, parts):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("B", [1, 8, 32])
 @pytest.mark.parametrize("seq", [128, 512, 2048])
-def test_script_default_sweep(gpu, B, seq):
+def test_script_default_sweep(gpu, dtype, B, seq):
     # benchmark_decoding.py's default sweep: batch sizes 1/8/32 x sequence lengths
-    # 128/512/2048, 16 heads over 8 kv heads, head_dim 128, block_size 256, a
-    # scattered table over a pool of exactly the blocks needed
-    case = pi.make_case(B, seq, 16, 8, 128, 256, dtype="bf16", seed=B * 10000 + seq)
-    say(f"script sweep B={B} seq={seq}")
+    # 128/512/2048, 16 heads over 8 kv heads, head_dim 128, block_size 256, fp16
+    # values, a scattered table over a pool of exactly the blocks needed
+    case = pi.make_case(B, seq, 16, 8, 128, 256, dtype=dtype, seed=B * 10000 + seq)
+    say(f"script sweep {dtype} B={B} seq={seq}")
     out = run_gpu(case, gpu)
-    assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"sweep B={B} seq={seq}")
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"sweep B={B} seq={seq}")
+
+
+def built(dtype, d, G):
+    # the (dtype, head dim, group size) combinations the library has kernels for
+    if d == 256:
+        return G <= (2 if dtype == "f32" else 8)
+    return True
+
+
+HEAD_DIM_CASES = [
+    # B, lens, H, Hkv, bs, holes
+    (3, [1, 100, 700], 32, 8, 16, [(2, 5)]),
+    (2, [300, 47], 16, 8, 256, []),
+    (2, [129, 1000], 8, 8, 32, [(1, 3)]),
+    (2, [250, 33], 64, 8, 16, []),
+    (2, [90, 500], 32, 2, 64, []),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("shape", HEAD_DIM_CASES)
+@pytest.mark.parametrize("parts", [0, 1, 5])
+def test_head_dims(gpu, dtype, d, shape, parts):
+    B, lens, H, Hkv, bs, holes = shape
+    if not built(dtype, d, H // Hkv):
+        pytest.skip(f"no kernel for {dtype} d={d} G={H // Hkv}: returns PA_ERR_UNSUPPORTED")
+    max_blocks = max(math.ceil(n / bs) for n in lens) + 1
+    need = sum(math.ceil(n / bs) for n in lens)
+    case = pi.make_case(B, lens, H, Hkv, d, bs, dtype=dtype, seed=d + bs + sum(lens),
+                        max_blocks=max_blocks, pool=need + 3, holes=holes)
+    say(f"head_dim {d} {dtype} lens {lens} H={H} Hkv={Hkv} bs={bs} P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"d={d} P={parts}")
+    poisoned = pi.poison_unused(case)
+    clean = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    clean.block_tables = poisoned.block_tables
+    a = run_gpu(clean, gpu, num_partitions=parts)
+    b = run_gpu(poisoned, gpu, num_partitions=parts)
+    assert torch.equal(a, b)
+
+
+def test_unbuilt_shape_is_rejected(gpu):
+    case = pi.make_case(1, 40, 128, 8, 256, 16, dtype="bf16", seed=1)
+    d = DeviceCase(case, gpu)
+    out = torch.empty_like(d.q)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode(out, *d.args(), None)
+    assert e.value.code == pa.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+@pytest.mark.parametrize("parts", [0, 1])
+def test_workload_shapes_in_fp16(gpu, cid, parts):
+    c = pi.CONFIGS[cid]
+    case = pi.make_case(c["B"], c["ctx"], c["H"], c["Hkv"], c["d"], c["bs"], dtype="f16",
+                        seed=500 + cid, pool=c["pool"])
+    say(f"workload {cid} shape in fp16, P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    assert_close(to_f64(out), oracle.decode_case(case), "f16", f"fp16 workload {cid}")
+
+    nbytes = pa.pa_workspace_bytes(case.batch, c["H"], c["d"], 8)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    out2 = run_gpu(case, gpu, num_partitions=8, workspace=(ws, nbytes))
+    assert_close(to_f64(out2), oracle.decode_case(case), "f16", f"fp16 workload {cid} 2-kernel")
