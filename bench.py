@@ -94,10 +94,7 @@ class Workload:
                                           self.cus) if num_partitions == 0
                   else num_partitions)
         tiles = c.max_blocks * c.block_size // 16   # partitions split 16-token tiles
-        self.P = min(self.P, tiles)
-        if self.P > 1:
-            per = math.ceil(tiles / self.P)
-            self.P = math.ceil(tiles / per)
+        self.P = max(1, min(self.P, tiles))
         self.num_partitions = num_partitions
         self.lib = pa.load()
 

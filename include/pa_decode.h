@@ -82,14 +82,24 @@ enum {
 };
 
 /*
+ * Partitions.  With P partitions, sequence b's n_b = ceil(context_lens[b] / 16)
+ * tiles of 16 tokens are dealt out in turn: partition p takes tiles p, p + P,
+ * p + 2P, ... below n_b.  The partitions of a sequence so differ by at most
+ * one tile whatever its length, and a batch of short contexts in a wide table
+ * still keeps every partition busy; when n_b < P the last P - n_b partitions
+ * of b are empty.  (The merge is a sum over the partitions' tokens, so they
+ * need not be contiguous.)
+ *
  * One decode step (the signature the docs page's kernel launch wraps:
  * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
  * shape parameters).  Picks the number of context partitions P with
  * pa_choose_partitions for the current device.  P == 1 runs one kernel that
  * writes out directly.  P > 1 runs the split kernel in its fused form: every
- * workgroup writes its partition's (max, sum, weighted values) to a
- * library-owned workspace and takes an atomic ticket; the last workgroup of
- * each (sequence, kv head) merges the P partials and writes out.  The partials
+ * workgroup of a non-empty partition writes its (max, sum, weighted values) to
+ * a library-owned workspace and takes an atomic ticket; the last workgroup of
+ * each (sequence, kv head) merges those partials and writes out.  A sequence
+ * with at most one non-empty partition is written directly by partition 0
+ * (zeros for an empty sequence); empty partitions do nothing.  The partials
  * buffer and the ticket buffer (zeroed when allocated; every call leaves its
  * tickets zero) are allocated on first need per (device, stream) and grown
  * when larger ones are needed (growing synchronises `stream` once).  Calls on
@@ -105,9 +115,7 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
 /*
  * pa_decode with the choices exposed.
  *   num_partitions   0 = heuristic (as pa_decode), 1 = single pass, n > 1 =
- *                    split each sequence's T tiles into n partitions of
- *                    ceil(T / n) tiles (n reduced to ceil(T / ceil(T / n)) so
- *                    none is empty by construction).
+ *                    P = min(n, T) partitions, split as above.
  *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
  *                    treated like -1 instead of being read (a guard against
  *                    out-of-range ids).
@@ -135,8 +143,9 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
  * then, from the next 256-byte boundary, [B][H][P][d] float sums.  An empty
  * partition stores
  * (-1e30, 0, zeros).  pa_merge_partials combines them into out.
- * Partition p covers tiles [p * ceil(T / P), (p + 1) * ceil(T / P)).
- * num_partitions must be >= 1 and is used as given (P = num_partitions).
+ * Partitions are split as above; every partition, empty ones included,
+ * writes its slot.  num_partitions must be >= 1 and is used as given
+ * (P = num_partitions).
  */
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_tables, const int32_t *context_lens, int B, int H,
@@ -154,9 +163,8 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
  * they already cover the device (>= num_cus) it returns 1.  Otherwise it
  * splits each unit's T tiles into enough partitions to give about num_cus
- * workgroups, keeping at least 8 tiles (128 tokens) per partition, then evens
- * the partitions out.  Returns >= 1 (1 for non-positive inputs or block_size
- * below 16).
+ * workgroups, keeping at least 8 tiles (128 tokens) per partition of a full
+ * row.  Returns >= 1 (1 for non-positive inputs or block_size below 16).
  */
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
 

@@ -153,22 +153,26 @@ int library_buffers(int dev, hipStream_t stream, size_t partial_bytes, size_t nu
     return PA_OK;
 }
 
-int run_main(const Params &p, int dtype, int d, int G, int mode, hipStream_t stream) {
-    const long long groups = (long long)p.Hkv * p.B * p.P;
-    if (groups > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-    hipError_t e;
-    switch (dtype) {
-        case PA_DTYPE_BF16:
-            e = launch_decode<PA_DTYPE_BF16>(p, d, G, mode, (int)groups, stream);
-            break;
-        case PA_DTYPE_F16:
-            e = launch_decode<PA_DTYPE_F16>(p, d, G, mode, (int)groups, stream);
-            break;
-        default:
-            e = launch_decode<PA_DTYPE_F32>(p, d, G, mode, (int)groups, stream);
-            break;
+// The decode kernel over all B sequences, in launches of at most kMaxGridY.
+int run_main(Params p, int dtype, int d, int G, int mode, hipStream_t stream) {
+    for (int b0 = 0; b0 < p.B; b0 += kMaxGridY) {
+        const int nseq = p.B - b0 < kMaxGridY ? p.B - b0 : kMaxGridY;
+        p.b0 = b0;
+        hipError_t e;
+        switch (dtype) {
+            case PA_DTYPE_BF16:
+                e = launch_decode<PA_DTYPE_BF16>(p, d, G, mode, nseq, stream);
+                break;
+            case PA_DTYPE_F16:
+                e = launch_decode<PA_DTYPE_F16>(p, d, G, mode, nseq, stream);
+                break;
+            default:
+                e = launch_decode<PA_DTYPE_F32>(p, d, G, mode, nseq, stream);
+                break;
+        }
+        if (e != hipSuccess) return PA_ERR_HIP;
     }
-    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+    return PA_OK;
 }
 
 int run_merge(void *out, void *ws, int B, int H, int P, int d, int dtype, hipStream_t stream) {
@@ -217,15 +221,16 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.counters = nullptr;
     p.tok_bytes = Hkv * d * esize;
     p.blk_bytes = (long long)block_size * p.tok_bytes;
-    p.pool = pool;
+    // ids are int32: a guard at or beyond 2^31 only has to skip negative ids
+    p.pool_limit = pool > 0 && pool < 0x7FFFFFFF ? (unsigned)pool : 0x7FFFFFFFu;
     p.B = B;
+    p.b0 = 0;
     p.H = H;
     p.Hkv = Hkv;
     p.max_blocks = max_blocks;
     p.P = P;
     p.tiles_log2 = log2_int(block_size / kTile);
     p.max_tiles = table_tiles(max_blocks, block_size);
-    p.bpp = (p.max_tiles + P - 1) / P;
     p.qk_scale = scale * kLog2e;
     return p;
 }
@@ -237,12 +242,11 @@ void attach_workspace(Params &p, void *ws, int d) {
     p.part_acc = reinterpret_cast<float *>(base + l.acc);
 }
 
-// P reduced so that no partition of a row of `tiles` tiles is empty.
-int even_partitions(int tiles, int P) {
-    if (P < 1) P = 1;
+// P limited to [1, tiles]: with at most one partition per tile, a full table
+// row leaves no partition empty.
+int clamp_partitions(int tiles, int P) {
     if (P > tiles) P = tiles;
-    const int per = (tiles + P - 1) / P;
-    return (tiles + per - 1) / per;
+    return P < 1 ? 1 : P;
 }
 
 }  // namespace
@@ -259,8 +263,7 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
     const long long cap = tiles / kMinTilesPerPartition;
     if (P > cap) P = cap;
     if (P > kMaxPartitions) P = kMaxPartitions;
-    if (P < 1) P = 1;
-    return even_partitions((int)tiles, (int)P);
+    return clamp_partitions((int)tiles, (int)P);
 }
 
 size_t pa_workspace_bytes(int B, int H, int d, int num_partitions) {
@@ -310,7 +313,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         if (cus < 0) return cus;
         P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
     } else {
-        P = even_partitions(table_tiles(max_blocks, block_size), num_partitions);
+        P = clamp_partitions(table_tiles(max_blocks, block_size), num_partitions);
     }
     if (P > kMaxPartitions) return PA_ERR_UNSUPPORTED;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,

@@ -39,12 +39,12 @@ struct Params {
     float *part_acc;    // [B][H][P][d]
     int *counters;      // [B][Hkv] arrival tickets (fused mode), zero between calls
     long long blk_bytes;  // bytes per physical block: block_size * Hkv * d * esize
-    long long pool;       // > 0: ids >= pool are skipped
+    unsigned pool_limit;  // table entries >= pool_limit (as unsigned: -1 too) are skipped
     int tok_bytes;        // bytes between tokens of a block: Hkv * d * esize
     int B, H, Hkv, max_blocks, P;
+    int b0;               // first sequence of this launch (grid y covers b0 ..)
     int tiles_log2;       // log2(block_size / 16): tiles per physical block
     int max_tiles;        // max_blocks * block_size / 16
-    int bpp;              // tiles per partition
     float qk_scale;       // scale * log2(e)
 };
 
@@ -67,11 +67,15 @@ constexpr bool shape_built(int dtype, int d, int G) {
     return true;
 }
 
-// Launch the decode kernel for element type DT on `groups` workgroups of
-// kWavesPerGroup waves (shape_built(DT, d, G) must hold), or the merge kernel
-// on one wave per (b, h).  Return the launch's hipGetLastError().
+// Sequences per decode launch: the grid's y extent.
+constexpr int kMaxGridY = 65535;
+
+// Launch the decode kernel for element type DT on a (Hkv, nseq, P) grid of
+// kWavesPerGroup-wave workgroups covering sequences p.b0 .. p.b0 + nseq - 1
+// (shape_built(DT, d, G) must hold), or the merge kernel on one wave per
+// (b, h).  Return the launch's hipGetLastError().
 template <int DT>
-hipError_t launch_decode(const Params &p, int d, int G, int mode, int groups,
+hipError_t launch_decode(const Params &p, int d, int G, int mode, int nseq,
                          hipStream_t stream);
 template <int DT>
 hipError_t launch_merge(const MergeParams &mp, int groups, hipStream_t stream);

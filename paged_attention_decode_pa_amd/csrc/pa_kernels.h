@@ -352,22 +352,27 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr int KL = Geo::kKLoads, VE = Geo::kVElems, VW = Geo::kVWords;
     constexpr int VLD = Geo::kVLoads, VWIDTH = Geo::kVWidth;
 
-    const int wg = blockIdx.x;
-    const int kvh = wg % p.Hkv;
-    const int b = (wg / p.Hkv) % p.B;
-    const int part = wg / (p.Hkv * p.B);
+    // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
+    const int kvh = blockIdx.x;
+    const int b = p.b0 + blockIdx.y;
+    const int part = blockIdx.z;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
     const int lane = threadIdx.x % kWave;
     const int c16 = lane & 15;  // MFMA column / token of the tile for K
     const int g = lane >> 4;    // MFMA row group: tokens 4g..4g+3 for V
 
-    const int lo = part * p.bpp;
-    const int first = lo + wave;  // this wave's tiles: first, first + NW, ...
+    // Partition p of a sequence takes its tiles p, p + P, p + 2P, ...; wave w
+    // of the partition takes every NW-th of those, starting at the w-th.  For
+    // any context length the partitions differ by at most one tile, and which
+    // tiles a wave owns does not depend on the length, so its first table
+    // entries are fetched before the length has arrived.
+    const int first = part + p.P * wave;  // this wave's tiles: first + stride * i
+    const int stride = p.P * NW;
     const int32_t *trow = p.table + (long long)b * p.max_blocks;
     // Table entry of the block holding the wave's i-th tile, the read clamped
     // into the row so it always stays in bounds (entries past the context are
     // read, never used).
-    auto tile_of = [&](int i) -> int { return first + NW * i; };
+    auto tile_of = [&](int i) -> int { return first + stride * i; };
     auto table_at = [&](int i) -> int {
         const int e = tile_of(i) >> p.tiles_log2;
         return trow[e < p.max_blocks ? e : p.max_blocks - 1];
@@ -386,9 +391,18 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     for (int m = 0; m < KL; ++m) qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
 
     ctx = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
-    const int ntiles = (ctx + kTile - 1) / kTile;
-    const int hi = min(lo + p.bpp, ntiles);
-    const int nw = hi > first ? (hi - first + NW - 1) / NW : 0;
+    const int ntiles = (int)(((unsigned)ctx + kTile - 1) / kTile);
+    // Partitions holding a tile (the first min(n, P)); the fused merge waits
+    // for exactly these.
+    const int busy = min(ntiles, p.P);
+    // One busy partition (or none) writes the output itself, as a single pass;
+    // in the fused mode a partition without tiles adds nothing to the merge
+    // and writes nothing (partition 0 of an empty sequence writes zeros).
+    // Such a partition still runs the (empty) prologue and epilogue: an early
+    // exit that depends on the context length would let the compiler hold
+    // back the query and table loads until that length has arrived.
+    const bool direct = MODE == kSingle || (MODE == kFused && busy <= 1);
+    const bool silent = MODE == kFused && part >= max(busy, 1);
 
     // Per-lane byte offsets inside one tile's rows of head kvh; never change.
     const unsigned koff = c16 * p.tok_bytes + 16 * g;
@@ -410,12 +424,13 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         for (int e = 0; e < VE; ++e) st.acc[h][e] = 0.f;
 
     // Live tokens of the wave's i-th tile given its block's table entry: 0 past
-    // the wave's range and for -1 (or out-of-pool) entries.
+    // the context and for -1 (or out-of-pool) entries.
+    // (Negative ids compare above any pool limit as unsigned.)
     auto live_tokens = [&](int i, int id) -> int {
         const int j = tile_of(i);
-        if (j >= hi || id < 0 || (p.pool > 0 && id >= p.pool)) return 0;
         const int rem = ctx - j * kTile;
-        return rem < kTile ? rem : kTile;
+        const int n = rem < kTile ? rem : kTile;
+        return (j < ntiles && (unsigned)id < p.pool_limit) ? n : 0;
     };
     // Loads of the wave's i-th tile: its rows start at the block's base plus
     // the tile's place inside the block.
@@ -434,29 +449,33 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
                 load_words<VWIDTH>(rv, voff[r][s], vd[r] + s * (VWIDTH / 4));
     };
 
-    if (nw > 0) {
-        // DEPTH tiles in flight: slot s of group k holds the wave's tile kDEPTH + s.
-        u32x4 kr[DEPTH][KL];
-        unsigned vr[DEPTH][4][VW];
-        int nl[DEPTH];
+    // DEPTH tiles in flight: slot s of group k holds the wave's tile kDEPTH + s.
+    // The first group is issued and consumed even by a wave with no tile: its
+    // descriptors are empty, so the loads return zeros without a memory access
+    // and the masked update leaves the state as it is.  Doing so keeps every
+    // use of the query and table loads unconditional, so the compiler issues
+    // them together with the context-length load instead of after it.
+    u32x4 kr[DEPTH][KL];
+    unsigned vr[DEPTH][4][VW];
+    int nl[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+        nl[s] = live_tokens(s, raw0[s]);
+        issue(kr[s], vr[s], s, raw0[s], nl[s]);
+    }
+    int k = 0;
+    do {
+        int nid[DEPTH];
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) nid[s] = table_at((k + 1) * DEPTH + s);
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-            nl[s] = live_tokens(s, raw0[s]);
-            issue(kr[s], vr[s], s, raw0[s], nl[s]);
+            consume_tile<DT, D, G>(st, kr[s], vr[s], qr, p.qk_scale, g, nl[s]);
+            nl[s] = live_tokens((k + 1) * DEPTH + s, nid[s]);
+            issue(kr[s], vr[s], (k + 1) * DEPTH + s, nid[s], nl[s]);
         }
-        const int ngroups = (nw + DEPTH - 1) / DEPTH;
-        for (int k = 0; k < ngroups; ++k) {
-            int nid[DEPTH];
-#pragma unroll
-            for (int s = 0; s < DEPTH; ++s) nid[s] = table_at((k + 1) * DEPTH + s);
-#pragma unroll
-            for (int s = 0; s < DEPTH; ++s) {
-                consume_tile<DT, D, G>(st, kr[s], vr[s], qr, p.qk_scale, g, nl[s]);
-                nl[s] = live_tokens((k + 1) * DEPTH + s, nid[s]);
-                issue(kr[s], vr[s], (k + 1) * DEPTH + s, nid[s], nl[s]);
-            }
-        }
-    }
+        ++k;
+    } while (tile_of(k * DEPTH) < ntiles);  // group k still holds a live tile
 
     // ---- merge the 4 row groups of the wave -----------------------------------
     // The (m, l) of row g and head h sit in the lanes of row g whose column is
@@ -507,7 +526,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             o1 = fmaf(sm_acc[w][h][e + 1], f, o1);
         }
         const long long bh = (long long)b * p.H + kvh * G + h;
-        if constexpr (MODE == kSingle) {
+        if (silent) {
+            // nothing to write
+        } else if (direct) {
             const float inv = L > 0.f ? 1.f / L : 0.f;
             store_pair<DT>(p.out, bh * D + e, o0 * inv, o1 * inv);
         } else if constexpr (MODE == kPartials) {
@@ -522,16 +543,18 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     }
 
     if constexpr (MODE == kFused) {
+        if (direct || silent) return;
         // Publish this partition (its coherent stores complete before the
-        // barrier), take a ticket; the last of the P workgroups of (b, kvh)
-        // merges all partitions and resets the ticket for the next call.
+        // barrier), take a ticket; the last of the `busy` workgroups of
+        // (b, kvh) merges their partitions and resets the ticket for the next
+        // call.
         __shared__ int sm_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
             const int prev = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1,
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sm_last = prev == p.P - 1;
+            sm_last = prev == busy - 1;
         }
         __syncthreads();
         if (sm_last) {
@@ -539,7 +562,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
                 const int h = idx / (D / 2), e = 2 * (idx % (D / 2));
                 const long long bh = (long long)b * p.H + kvh * G + h;
                 const float2 o = merge_partitions<true>(p.part_ml + bh * p.P,
-                                                        p.part_acc + bh * p.P * D + e, p.P, D);
+                                                        p.part_acc + bh * p.P * D + e, busy, D);
                 store_pair<DT>(p.out, bh * D + e, o.x, o.y);
             }
             if (threadIdx.x == 0)
@@ -562,10 +585,10 @@ __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
 }
 
 template <int DT, int D, int G, int MODE>
-hipError_t launch_instance(const Params &p, int groups, hipStream_t stream) {
+hipError_t launch_instance(const Params &p, int nseq, hipStream_t stream) {
     if constexpr (shape_built(DT, D, G)) {
         hipLaunchKernelGGL((pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
-                           dim3(groups), dim3(kWavesPerGroup * kWave), 0, stream, p);
+                           dim3(p.Hkv, nseq, p.P), dim3(kWavesPerGroup * kWave), 0, stream, p);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;
@@ -573,33 +596,33 @@ hipError_t launch_instance(const Params &p, int groups, hipStream_t stream) {
 }
 
 template <int DT, int D, int MODE>
-hipError_t dispatch_g(const Params &p, int G, int groups, hipStream_t stream) {
+hipError_t dispatch_g(const Params &p, int G, int nseq, hipStream_t stream) {
     switch (G) {
-        case 1: return launch_instance<DT, D, 1, MODE>(p, groups, stream);
-        case 2: return launch_instance<DT, D, 2, MODE>(p, groups, stream);
-        case 4: return launch_instance<DT, D, 4, MODE>(p, groups, stream);
-        case 8: return launch_instance<DT, D, 8, MODE>(p, groups, stream);
-        case 16: return launch_instance<DT, D, 16, MODE>(p, groups, stream);
+        case 1: return launch_instance<DT, D, 1, MODE>(p, nseq, stream);
+        case 2: return launch_instance<DT, D, 2, MODE>(p, nseq, stream);
+        case 4: return launch_instance<DT, D, 4, MODE>(p, nseq, stream);
+        case 8: return launch_instance<DT, D, 8, MODE>(p, nseq, stream);
+        case 16: return launch_instance<DT, D, 16, MODE>(p, nseq, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int DT, int D>
-hipError_t dispatch_mode(const Params &p, int G, int mode, int groups, hipStream_t stream) {
+hipError_t dispatch_mode(const Params &p, int G, int mode, int nseq, hipStream_t stream) {
     switch (mode) {
-        case kSingle: return dispatch_g<DT, D, kSingle>(p, G, groups, stream);
-        case kPartials: return dispatch_g<DT, D, kPartials>(p, G, groups, stream);
-        default: return dispatch_g<DT, D, kFused>(p, G, groups, stream);
+        case kSingle: return dispatch_g<DT, D, kSingle>(p, G, nseq, stream);
+        case kPartials: return dispatch_g<DT, D, kPartials>(p, G, nseq, stream);
+        default: return dispatch_g<DT, D, kFused>(p, G, nseq, stream);
     }
 }
 
 template <int DT>
-hipError_t launch_decode(const Params &p, int d, int G, int mode, int groups,
+hipError_t launch_decode(const Params &p, int d, int G, int mode, int nseq,
                          hipStream_t stream) {
     switch (d) {
-        case 64: return dispatch_mode<DT, 64>(p, G, mode, groups, stream);
-        case 128: return dispatch_mode<DT, 128>(p, G, mode, groups, stream);
-        case 256: return dispatch_mode<DT, 256>(p, G, mode, groups, stream);
+        case 64: return dispatch_mode<DT, 64>(p, G, mode, nseq, stream);
+        case 128: return dispatch_mode<DT, 128>(p, G, mode, nseq, stream);
+        case 256: return dispatch_mode<DT, 256>(p, G, mode, nseq, stream);
         default: return hipErrorInvalidValue;
     }
 }

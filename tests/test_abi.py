@@ -43,7 +43,7 @@ def test_strerror_covers_codes():
     (4, 8, 128, 16, 256, 8),      # 32 units -> 8 partitions of 16 tiles
     (1, 8, 1024, 16, 256, 32),    # 8 units -> 32 partitions of 32 tiles
     (32, 8, 1024, 16, 256, 1),    # 256 units already fill 256 CUs
-    (1, 1, 100, 16, 256, 12),     # capped at 100 // 8 = 12, evened to 12 (9 tiles each)
+    (1, 1, 100, 16, 256, 12),     # capped at 100 // 8 = 12 (runs of 8 or 9 tiles)
     (1, 8, 7, 16, 256, 1),
     (0, 8, 10, 16, 256, 1),
     (3, 8, 1000, 16, 0, 1),
@@ -63,12 +63,12 @@ def test_choose_partitions_properties():
                 for cus in (80, 256, 304):
                     P = pa.pa_choose_partitions(B, Hkv, mb, 16, cus)
                     assert 1 <= P <= max(1, mb)
-                    bpp = math.ceil(mb / P)
-                    # no empty partition by construction
-                    assert (P - 1) * bpp < mb
                     if P > 1:
-                        assert bpp >= 8
+                        # every partition of a full row gets at least 8 tiles
+                        assert mb // P >= 8
                         assert B * Hkv < cus
+                        # and about one workgroup per compute unit, not more
+                        assert B * Hkv * (P - 1) < cus
 
 
 def test_workspace_bytes():

@@ -387,3 +387,96 @@ def test_workload_shapes_in_fp16(gpu, cid, parts):
     ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
     out2 = run_gpu(case, gpu, num_partitions=8, workspace=(ws, nbytes))
     assert_close(to_f64(out2), oracle.decode_case(case), "f16", f"fp16 workload {cid} 2-kernel")
+
+
+WIDE_TABLE_CASES = [
+    # B, lens, table width in blocks: contexts far shorter than the table row
+    (6, [0, 1, 17, 300, 1000, 5000], 1024),
+    (8, [16, 16, 16, 16, 16, 16, 16, 16], 512),
+    (3, [2047, 2048, 2049], 512),
+    (1, [130], 4096),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WIDE_TABLE_CASES)
+@pytest.mark.parametrize("parts", [0, 3, 32, 4096])
+def test_short_contexts_in_wide_table(gpu, dtype, shape, parts):
+    # partitions split each sequence's own live tiles, so here most runs are
+    # short and many partitions of short sequences are empty
+    B, lens, width = shape
+    need = sum(math.ceil(n / 16) for n in lens)
+    case = pi.make_case(B, lens, 32, 8, 128, 16, dtype=dtype, seed=width + sum(lens),
+                        max_blocks=width, pool=need + 4)
+    say(f"wide table {width} lens {lens} {dtype} P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"wide P={parts}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert (out[b].float() == 0).all()
+
+
+def expected_partials(case, P):
+    """Per-partition (max, sum, weighted sum) from the header's split rule,
+    computed directly in fp64: partition p of sequence b (n tiles) holds the
+    tokens of tiles p, p + P, p + 2P, ... below n; with scores
+    s = scale * q.K * log2(e): m = max s, l = sum 2^(s - m),
+    O = sum 2^(s - m) V; empty partitions give (-1e30, 0, 0)."""
+    B, H, d = case.q.shape
+    G = H // case.num_kv_heads
+    bs = case.block_size
+    m = np.full((B, H, P), -1e30)
+    l = np.zeros((B, H, P))
+    o = np.zeros((B, H, P, d))
+    for b in range(B):
+        ctx = int(case.context_lens[b])
+        n = (ctx + 15) // 16
+        for p in range(P):
+            toks = [t for j in range(p, n, P) for t in range(j * 16, min(j * 16 + 16, ctx))
+                    if case.block_tables[b, t // bs] >= 0]
+            if not toks:
+                continue
+            for h in range(H):
+                kvh = h // G
+                K = np.array([case.k_cache[case.block_tables[b, t // bs], t % bs, kvh]
+                              for t in toks], dtype=np.float64)
+                V = np.array([case.v_cache[case.block_tables[b, t // bs], t % bs, kvh]
+                              for t in toks], dtype=np.float64)
+                s = float(case.scale) * (K @ case.q[b, h].astype(np.float64)) / math.log(2)
+                m[b, h, p] = s.max()
+                w = np.exp2(s - s.max())
+                l[b, h, p] = w.sum()
+                o[b, h, p] = w @ V
+    return m, l, o
+
+
+def test_partials_follow_documented_split(gpu):
+    case = pi.make_case(4, [83, 16, 0, 700], 8, 2, 128, 16, dtype="f32", seed=77,
+                        max_blocks=50, pool=60)
+    P = 8
+    d = DeviceCase(case, gpu)
+    nbytes = pa.pa_workspace_bytes(case.batch, 8, 128, P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    say("partials layout and split rule")
+    pa.pa_decode_partials(*d.args(), P, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    ml_bytes = case.batch * 8 * P * 8
+    acc_off = (ml_bytes + 255) // 256 * 256
+    host = ws.cpu()
+    ml = host[:ml_bytes].view(torch.float32).view(case.batch, 8, P, 2).double().numpy()
+    acc = host[acc_off:acc_off + case.batch * 8 * P * 128 * 4].view(torch.float32)
+    acc = acc.view(case.batch, 8, P, 128).double().numpy()
+    m, l, o = expected_partials(case, P)
+    empty = l == 0
+    assert (ml[..., 0][empty] == np.float32(-1e30)).all() and (ml[..., 1][empty] == 0).all()
+    assert (acc[empty] == 0).all()
+    live = ~empty
+    assert np.abs(ml[..., 0][live] - m[live]).max() <= 1e-4 * max(1.0, np.abs(m[live]).max())
+    assert (np.abs(ml[..., 1][live] - l[live]) <= 1e-4 * l[live]).all()
+    vmax = np.abs(case.v_cache).max()
+    err = np.abs(acc - o).max(axis=-1)
+    assert (err[live] <= 1e-4 * l[live] * vmax).all()
+    # sequence 2 is empty; sequence 1 has one tile (partition 0 only);
+    # sequence 0 has 6 tiles (partitions 0-5), sequence 3 has 44 (all 8)
+    assert empty[2].all() and (~empty[1, :, 0]).all() and empty[1, :, 1:].all()
+    assert (~empty[0, :, :6]).all() and empty[0, :, 6:].all() and (~empty[3]).all()
