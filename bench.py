@@ -58,24 +58,31 @@ def parse():
                     help="CPU work budget of the oracle baseline (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (counter scale)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline: single pass vs split-KV over batch 1 and 4 "
+                         "and KV lengths 512..16384 (the design note's sweep)")
     return ap.parse_args()
+
+
+TORCH_DTYPES = {"bf16": "bfloat16", "f16": "float16", "f32": "float32"}
+# parity tolerances: |gpu - oracle| <= atol + rtol * |oracle| (fp32: max abs)
+TOLERANCE = {"f32": (1e-5, 0.0), "bf16": (2e-3, 1e-2), "f16": (5e-5, 2.0 ** -10)}
 
 
 class Workload:
     """N rotation copies of one workload's inputs on the device."""
 
-    def __init__(self, cid, dev, num_partitions=0, seed=None):
+    def __init__(self, case, dev, num_partitions=0):
         import torch
-        import pa_inputs as pi
         import paged_attention_decode_pa_amd as pa
 
-        self.cid = cid
-        self.case = pi.make_config_case(cid, seed)
+        self.case = case
         c = self.case
         self.bytes = c.algorithmic_bytes()
         self.ncopies = max(2, min(MAX_COPIES, math.ceil(ROTATION_BYTES / self.bytes)))
-        if c.dtype == "bf16":
-            conv = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+        if c.dtype != "f32":
+            tdt = getattr(torch, TORCH_DTYPES[c.dtype])
+            conv = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(tdt)
             q0, k0, v0 = conv(c.q_bits), conv(c.k_bits), conv(c.v_bits)
         else:
             q0, k0, v0 = (torch.from_numpy(x).to(dev) for x in (c.q, c.k_cache, c.v_cache))
@@ -179,21 +186,19 @@ def parity_gate(w):
     ref = oracle.decode_case(w.case)
     got = w.copies[0]["out"].float().cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
-    if w.case.dtype == "f32":
-        ok = err.max() <= 1e-5
-    else:
-        ok = bool((err <= 2e-3 + 1e-2 * np.abs(ref)).all())
+    atol, rtol = TOLERANCE[w.case.dtype]
+    ok = bool((err <= atol + rtol * np.abs(ref)).all())
     same = all(torch.equal(x["out"], w.copies[0]["out"]) for x in w.copies)
     return ok and same, float(err.max())
 
 
-def measure(cid, dev, steps, warmup, use_graph, num_partitions=0):
-    w = Workload(cid, dev, num_partitions)
+def measure(case, dev, steps, warmup, use_graph, num_partitions=0):
+    w = Workload(case, dev, num_partitions)
     for i in range(w.ncopies):
         w.step(i, None)
     ok, max_err = parity_gate(w)
     if not ok:
-        raise SystemExit(f"workload {cid}: parity gate FAILED (max err {max_err:.3e}); "
+        raise SystemExit(f"{case.name}: parity gate FAILED (max err {max_err:.3e}); "
                          "timing would be meaningless")
     t_step = time_region(w.step, steps, warmup, use_graph)
     return w, t_step, max_err
@@ -248,6 +253,57 @@ def cpu_baseline(cid, budget_s):
                 ms_per_step=round(per * 1e3, 3))
 
 
+# The flash-decoding-bench design note's sweep: decode steps (one query token)
+# at batch sizes 1 and 4 over KV lengths 512 .. 16384, fused single pass
+# against the KV-parallel split.  The note models plain multi-head attention
+# (no grouped-query heads) and gives no head count; 32 heads of 128 in fp16 are
+# used here, in 16-token blocks of a scattered table over a pool of exactly the
+# blocks needed.
+SWEEP_BATCHES = (1, 4)
+SWEEP_KV = (512, 1024, 2048, 4096, 8192, 16384)
+SWEEP_SHAPE = dict(H=32, Hkv=32, d=128, bs=16, dtype="f16")
+
+
+def sweep(dev, steps, warmup, use_graph):
+    import torch
+    import pa_inputs as pi
+    sh = SWEEP_SHAPE
+    points = []
+    for batch in SWEEP_BATCHES:
+        for kv in SWEEP_KV:
+            case = pi.make_case(batch, kv, sh["H"], sh["Hkv"], sh["d"], sh["bs"],
+                                dtype=sh["dtype"], seed=batch * 100000 + kv,
+                                name=f"{sh['dtype']} B={batch} ctx={kv} H={sh['H']} "
+                                     f"Hkv={sh['Hkv']} d={sh['d']} bs={sh['bs']}")
+            row = dict(batch=batch, kv_len=kv, algorithmic_bytes=case.algorithmic_bytes())
+            for label, parts in (("single", 1), ("split", 0)):
+                w, ts, err = measure(case, dev, steps, warmup, use_graph, parts)
+                row[f"{label}_partitions"] = w.P
+                row[f"{label}_us"] = round(ts * 1e6, 3)
+                row[f"{label}_GBps"] = round(w.bytes / ts / 1e9, 1)
+                row[f"{label}_max_abs_err"] = err
+                del w
+                torch.cuda.empty_cache()
+            row["split_speedup"] = round(row["single_us"] / row["split_us"], 3)
+            log(f"B={batch} kv={kv}: single {row['single_us']:.2f} us, split "
+                f"(P={row['split_partitions']}) {row['split_us']:.2f} us, "
+                f"speedup {row['split_speedup']:.2f}x")
+            points.append(row)
+    crossover = {}
+    for batch in SWEEP_BATCHES:
+        wins = [p["kv_len"] for p in points if p["batch"] == batch and p["split_speedup"] > 1]
+        crossover[str(batch)] = min(wins) if wins else None
+    return dict(
+        metric="decode step us, fused single pass vs split-KV (Flash-Decoding) with fused merge",
+        unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
+        dtype=sh["dtype"], data="synthetic",
+        config=dict(workload="design-note sweep: batch 1 and 4, KV 512..16384, one query "
+                             "token, multi-head", num_heads=sh["H"], num_kv_heads=sh["Hkv"],
+                    head_dim=sh["d"], block_size=sh["bs"],
+                    timing="HIP graph replay of K steps" if use_graph else "eager launches"),
+        crossover_kv_len=crossover, points=points)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -255,18 +311,23 @@ def main():
               "(the decode step has no multi-GPU path in this library)", file=sys.stderr)
         sys.exit(2)
     import torch
+    import pa_inputs as pi
     import paged_attention_decode_pa_amd as pa
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     pa.load()
     dev = torch.device("cuda:0")
     use_graph = not args.eager
+    if args.sweep:
+        print(json.dumps(sweep(dev, min(args.steps, 500), args.warmup, use_graph)), flush=True)
+        return
 
     per_config = []
     if not args.no_per_config:
         plan = [(c, 0) for c in (1, 2, 3, 4, 5) if c != args.workload] + [(4, 1), (5, 1)]
         for cid, parts in plan:
-            w, ts, err = measure(cid, dev, min(args.steps, 1000), args.warmup, use_graph, parts)
+            w, ts, err = measure(pi.make_config_case(cid), dev, min(args.steps, 1000),
+                                 args.warmup, use_graph, parts)
             per_config.append(dict(
                 workload=cid, name=w.case.name, partitions=w.P,
                 path="single-pass" if w.P == 1 else "split-KV + merge",
@@ -279,7 +340,8 @@ def main():
             del w
             torch.cuda.empty_cache()
 
-    w, t_step, err = measure(args.workload, dev, args.steps, args.warmup, use_graph)
+    w, t_step, err = measure(pi.make_config_case(args.workload), dev, args.steps, args.warmup,
+                             use_graph)
     gbs = w.bytes / t_step / 1e9
     log(f"headline workload {args.workload} P={w.P}: {t_step * 1e6:.2f} us/step {gbs:.0f} GB/s")
     if not w.single_launch():
@@ -314,7 +376,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if c.dtype == "bf16" else "f32",
+        "dtype": c.dtype,
         "data": "synthetic",
         "config": {
             "workload": c.name + (" split-KV (Flash-Decoding) + merge" if w.P > 1
