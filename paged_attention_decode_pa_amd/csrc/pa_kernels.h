@@ -278,27 +278,15 @@ __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, unsigned of
     }
 }
 
-// Float pair access at agent scope.  The split kernel's fused merge exchanges
+// Float pair store at agent scope.  The split kernel's fused merge exchanges
 // partials between workgroups that may run on different XCDs (each with its own
-// L2): these stores write through to the device-coherent level and these loads
-// read from it, so no L2 writeback or invalidate is needed.
+// L2): these stores write through to the device-coherent level and the merge
+// reads from it (kCoherent loads), so no L2 writeback or invalidate is needed.
 __device__ __forceinline__ void store_pair_coherent(float *p, float x0, float x1) {
     __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
                        __builtin_bit_cast(unsigned long long, make_float2(x0, x1)),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float2 load_pair_coherent(const float *p) {
-    return __builtin_bit_cast(
-        float2, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
-template <bool COHERENT>
-__device__ __forceinline__ float2 load_pair(const float *p) {
-    if constexpr (COHERENT) return load_pair_coherent(p);
-    else return *reinterpret_cast<const float2 *>(p);
-}
-
 // Combine the P partitions of (b, h) for head-dim elements e, e + 1 with the
 // rescale-and-sum rule, running over the partitions in order.  ml points at
 // the (max, sum) pairs of (b, h), acc at element e of its first partition;
@@ -307,7 +295,7 @@ __device__ __forceinline__ float2 load_pair(const float *p) {
 // before the first is used.  Reads past P are clamped to the last partition
 // and replaced by an empty partition (max -1e30, sum 0, zeros), which leaves
 // the running state as it is.
-template <int CHUNK, bool COHERENT>
+template <int CHUNK>
 __device__ __forceinline__ float2 merge_chunked(const float2 *ml, const float *acc, int P, int d) {
     float M = kMaxInit, L = 0.f, o0 = 0.f, o1 = 0.f;
     for (int q0 = 0; q0 < P; q0 += CHUNK) {
@@ -315,8 +303,8 @@ __device__ __forceinline__ float2 merge_chunked(const float2 *ml, const float *a
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
             const int q = q0 + j < P ? q0 + j : P - 1;
-            s[j] = load_pair<COHERENT>(reinterpret_cast<const float *>(ml + q));
-            a[j] = load_pair<COHERENT>(acc + (long long)q * d);
+            s[j] = ml[q];
+            a[j] = *reinterpret_cast<const float2 *>(acc + (long long)q * d);
         }
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
@@ -337,13 +325,103 @@ __device__ __forceinline__ float2 merge_chunked(const float2 *ml, const float *a
 
 // The chunk is the smallest of 4, 8, 16, 32 that holds P (32 beyond that), so
 // few partitions do not pay for loads of padding.
-template <bool COHERENT>
 __device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float *acc, int P,
                                                    int d) {
-    if (P <= 4) return merge_chunked<4, COHERENT>(ml, acc, P, d);
-    if (P <= 8) return merge_chunked<8, COHERENT>(ml, acc, P, d);
-    if (P <= 16) return merge_chunked<16, COHERENT>(ml, acc, P, d);
-    return merge_chunked<32, COHERENT>(ml, acc, P, d);
+    if (P <= 4) return merge_chunked<4>(ml, acc, P, d);
+    if (P <= 8) return merge_chunked<8>(ml, acc, P, d);
+    if (P <= 16) return merge_chunked<16>(ml, acc, P, d);
+    return merge_chunked<32>(ml, acc, P, d);
+}
+
+// Cache-policy bits (sc1) that make a buffer access agent-coherent: loads
+// read past this XCD's L2, which may hold stale copies of lines other XCDs
+// have rewritten since.
+constexpr int kCoherent = 16;
+
+// The fused merge of the `busy` partitions of (b, kvh) by one workgroup.  Each
+// (head, 4-element quad) of the group's output is shared by S threads; thread
+// `split` folds partitions split, split + S, ... (all of a chunk's loads in
+// flight at once), then the S partial states are folded together with an xor
+// butterfly, all with the rescale-and-sum rule.  S is chosen so that the
+// items fill the workgroup, which keeps each thread's loads few enough to
+// leave in one round trip; CH (the chunk) is the smallest power of two up to
+// 16 that holds a thread's share, so few partitions load no padding.
+template <int DT, int D, int G, int NW>
+constexpr int merge_split() {
+    constexpr int kThreads = NW * kWave, kItems = G * D / 4;
+    return kItems >= kThreads ? 1 : kThreads / kItems;
+}
+
+template <int DT, int D, int G, int NW, int CH>
+__device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int kvh, int busy) {
+    constexpr int kThreads = NW * kWave;
+    constexpr int kQuads = D / 4;
+    constexpr int kItems = G * kQuads;
+    constexpr int S = merge_split<DT, D, G, NW>();
+    static_assert(kItems % kThreads == 0 || kItems * S == kThreads,
+                  "every thread must take part in the butterfly");
+    const long long bh0 = (long long)b * p.H + kvh * G;
+    const __amdgpu_buffer_rsrc_t rml =
+        buffer_rsrc(reinterpret_cast<const char *>(p.part_ml + bh0 * p.P), G * p.P * 8);
+    const __amdgpu_buffer_rsrc_t racc =
+        buffer_rsrc(reinterpret_cast<const char *>(p.part_acc + bh0 * p.P * D), G * p.P * D * 4);
+    for (int t = threadIdx.x; t < kItems * S; t += kThreads) {
+        const int item = t / S, split = t % S;
+        const int h = item / kQuads, quad = item % kQuads;
+        float M = kMaxInit, L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int q0 = split; q0 < busy; q0 += S * CH) {
+            float2 sm[CH];
+            f32x4 ac[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int q = q0 + S * j < busy ? q0 + S * j : q0;  // clamped into range
+                sm[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rml, (h * p.P + q) * 8, 0, kCoherent));
+                ac[j] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               racc, ((h * p.P + q) * D + 4 * quad) * 4, 0, kCoherent));
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const bool live = q0 + S * j < busy;
+                const float mj = live ? sm[j].x : kMaxInit;
+                const float mn = fmaxf(M, mj);
+                const float fo = fast_exp2(M - mn);
+                const float fp = live ? fast_exp2(mj - mn) : 0.f;
+                L = L * fo + sm[j].y * fp;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = o[e] * fo + ac[j][e] * fp;
+                M = mn;
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < S; off <<= 1) {
+            const float M2 = __shfl_xor(M, off), L2 = __shfl_xor(L, off);
+            const float mn = fmaxf(M, M2);
+            const float f1 = fast_exp2(M - mn), f2 = fast_exp2(M2 - mn);
+            L = L * f1 + L2 * f2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = o[e] * f1 + __shfl_xor(o[e], off) * f2;
+            M = mn;
+        }
+        if (split == 0) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            const long long at = (bh0 + h) * D + 4 * quad;
+            store_pair<DT>(p.out, at, o[0] * inv, o[1] * inv);
+            store_pair<DT>(p.out, at + 2, o[2] * inv, o[3] * inv);
+        }
+    }
+}
+
+template <int DT, int D, int G, int NW>
+__device__ __forceinline__ void merge_group(const Params &p, int b, int kvh, int busy) {
+    constexpr int S = merge_split<DT, D, G, NW>();
+    const int share = (busy + S - 1) / S;  // partitions per thread
+    if (share <= 1) merge_group_chunked<DT, D, G, NW, 1>(p, b, kvh, busy);
+    else if (share <= 2) merge_group_chunked<DT, D, G, NW, 2>(p, b, kvh, busy);
+    else if (share <= 4) merge_group_chunked<DT, D, G, NW, 4>(p, b, kvh, busy);
+    else if (share <= 8) merge_group_chunked<DT, D, G, NW, 8>(p, b, kvh, busy);
+    else merge_group_chunked<DT, D, G, NW, 16>(p, b, kvh, busy);
 }
 
 template <int DT, int D, int G, int NW, int DEPTH, int MODE>
@@ -558,13 +636,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         }
         __syncthreads();
         if (sm_last) {
-            for (int idx = threadIdx.x; idx < G * (D / 2); idx += NW * kWave) {
-                const int h = idx / (D / 2), e = 2 * (idx % (D / 2));
-                const long long bh = (long long)b * p.H + kvh * G + h;
-                const float2 o = merge_partitions<true>(p.part_ml + bh * p.P,
-                                                        p.part_acc + bh * p.P * D + e, busy, D);
-                store_pair<DT>(p.out, bh * D + e, o.x, o.y);
-            }
+            merge_group<DT, D, G, NW>(p, b, kvh, busy);
             if (threadIdx.x == 0)
                 __hip_atomic_store(p.counters + b * p.Hkv + kvh, 0, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -578,7 +650,7 @@ template <int DT>
 __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
     const long long bh = blockIdx.x;
     for (int e = 2 * threadIdx.x; e < mp.d; e += 2 * kWave) {
-        const float2 o = merge_partitions<false>(mp.part_ml + bh * mp.P,
+        const float2 o = merge_partitions(mp.part_ml + bh * mp.P,
                                                  mp.part_acc + bh * mp.P * mp.d + e, mp.P, mp.d);
         store_pair<DT>(mp.out, bh * mp.d + e, o.x, o.y);
     }
