@@ -137,9 +137,12 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
  * The two halves of the split path, for callers that schedule them apart or
  * time them separately (Flash-Decoding's per-chunk pass and its merge).
  * pa_decode_partials runs only the split kernel: for every (b, h) and
- * partition p < P it writes the partition's running max (log2 units, i.e.
- * of scale * log2(e) * q.K), its normaliser and its unnormalised weighted sum
- * of V rows into `workspace`.  Layout: [B][H][P] float pairs (max, sum),
+ * partition p < P it writes a reference max m, the normaliser
+ * l = sum_t 2^(s_t - m) and the unnormalised weighted sum O = sum_t
+ * 2^(s_t - m) V_t over the partition's tokens t, with scores in log2 units
+ * (s_t = scale * log2(e) * q.K_t), into `workspace`; the partition's result is
+ * O / l.  m is within 8 of the largest score: max_t s_t - 8 <= m <= max_t s_t
+ * (up to fp32 rounding).  Layout: [B][H][P] float pairs (max, sum),
  * then, from the next 256-byte boundary, [B][H][P][d] float sums.  An empty
  * partition stores
  * (-1e30, 0, zeros).  pa_merge_partials combines them into out.

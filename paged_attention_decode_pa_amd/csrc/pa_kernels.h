@@ -23,7 +23,9 @@
 //   the scores of tokens 4g..4g+3 for head c % G.
 // * Online softmax per (row g, head): running max m and normaliser l in log2
 //   units (scale * log2 e is folded into one multiply), so each lane updates
-//   its own statistics from its 4 scores with no cross-lane max per tile.
+//   its own statistics from its 4 scores with no cross-lane max per tile.  The
+//   max is a reference that moves only when a score exceeds it by more than
+//   2^8 (a wave-wide vote), so most tiles skip the rescale of the state.
 // * V accumulate on the vector ALUs in fp32: lane (g, c) holds D / 16 elements
 //   of the V rows of tokens 4g..4g+3 and accumulates them for all G heads; the
 //   weights of the other heads come from neighbouring lanes by DPP broadcast.
@@ -50,6 +52,10 @@ namespace pa_detail {
 constexpr float kLog2e = 1.44269504088896340736f;
 // Start value of a running max: finite, so 2^(m - m') never sees inf - inf.
 constexpr float kMaxInit = -1.0e30f;
+// How far (log2 units) a score may exceed the running reference max before
+// the state is rescaled: weights stay <= 2^8, so the fp32 sums cannot overflow
+// (at most 2^8 per token, 2^30 tokens) and keep their relative precision.
+constexpr float kRescaleSlack = 8.0f;
 
 #ifndef PA_PIPELINE_DEPTH
 #define PA_PIPELINE_DEPTH 2
@@ -163,16 +169,14 @@ struct WaveState {
     float acc[G][VE];   // unnormalised sum of p * V for every head of the group
 };
 
-// One tile's scores, softmax update and V accumulation.  nlive = tokens of the
-// tile that take part (0..16); K/V slots at or past nlive were read as zeros
-// (they lie outside the tile's buffer range), so only their scores need
-// masking.
-template <int DT, int D, int G>
-__device__ __forceinline__ void consume_tile(WaveState<G, D / 16> &st, const u32x4 *kr,
-                                             const unsigned (*vw)[Geometry<DT, D>::kVWords],
-                                             const u32x4 *qr, float qk_scale, int g, int nlive) {
+// One tile's scores (q.K for its 16 tokens and the G heads, on the matrix
+// cores; softmax update and V accumulation follow in update_tile).  nlive =
+// tokens of the tile that take part (0..16); K/V slots at or past nlive were
+// read as zeros (they lie outside the tile's buffer range), so only their
+// scores need masking.
+template <int DT, int D>
+__device__ __forceinline__ f32x4 tile_scores(const u32x4 *kr, const u32x4 *qr) {
     using Geo = Geometry<DT, D>;
-    constexpr int VE = Geo::kVElems;
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DT == PA_DTYPE_BF16) {
 #pragma unroll
@@ -194,24 +198,43 @@ __device__ __forceinline__ void consume_tile(WaveState<G, D / 16> &st, const u32
                 c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr[m][j]),
                                                           __uint_as_float(qr[m][j]), c, 0, 0, 0);
     }
+    return c;
+}
+
+// The softmax update and V accumulation of one tile given its raw scores c
+// (tile_scores).
+template <int DT, int D, int G>
+__device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
+                                            const unsigned (*vw)[Geometry<DT, D>::kVWords],
+                                            float qk_scale, int g, int nlive) {
+    using Geo = Geometry<DT, D>;
+    constexpr int VE = Geo::kVElems;
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = (4 * g + r < nlive) ? c[r] * qk_scale : -INFINITY;
     const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    const float mn = fmaxf(st.m, bm);
-    const float alpha = fast_exp2(st.m - mn);
+    // The reference max m only moves (and l, acc are rescaled by 2^(m - m'))
+    // when some lane of the wave sees a score more than kRescaleSlack above
+    // its m; otherwise weights 2^(s - m) up to 2^kRescaleSlack are summed as
+    // they are.  The result is the same -- every state (m, l, acc) stands for
+    // acc / l whatever its m -- and the wave skips the rescale, and its wait
+    // for this tile's max, on almost every tile.
+    if (__builtin_amdgcn_ballot_w64(bm > st.m + kRescaleSlack) != 0) {
+        const float mn = fmaxf(st.m, bm);
+        const float alpha = fast_exp2(st.m - mn);
+        st.l *= alpha;
+        st.m = mn;
+        static_for<G>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const float a = group_bcast<G, h>(alpha);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) st.acc[h][e] *= a;
+        });
+    }
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - mn);
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    st.m = mn;
-
-    static_for<G>([&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        const float a = group_bcast<G, h>(alpha);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) st.acc[h][e] *= a;
-    });
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - st.m);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float vf[VE];
@@ -546,9 +569,13 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         int nid[DEPTH];
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) nid[s] = table_at((k + 1) * DEPTH + s);
+        // (each tile's scores right before its update: computing the group's
+        // scores first makes the first update wait for the later tiles' K
+        // rows as well, since loads complete in order, and measures slower)
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-            consume_tile<DT, D, G>(st, kr[s], vr[s], qr, p.qk_scale, g, nl[s]);
+            update_tile<DT, D, G>(st, tile_scores<DT, D>(kr[s], qr), vr[s], p.qk_scale, g,
+                                  nl[s]);
             nl[s] = live_tokens((k + 1) * DEPTH + s, nid[s]);
             issue(kr[s], vr[s], (k + 1) * DEPTH + s, nid[s], nl[s]);
         }
