@@ -577,6 +577,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             update_tile<DT, D, G>(st, tile_scores<DT, D>(kr[s], qr), vr[s], p.qk_scale, g,
                                   nl[s]);
             nl[s] = live_tokens((k + 1) * DEPTH + s, nid[s]);
+            // (tiles past the context are issued too, with empty ranges: a
+            // branch here measures slower than the loads it would save)
             issue(kr[s], vr[s], (k + 1) * DEPTH + s, nid[s], nl[s]);
         }
         ++k;
@@ -584,8 +586,11 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 
     // ---- merge the 4 row groups of the wave -----------------------------------
     // The (m, l) of row g and head h sit in the lanes of row g whose column is
-    // h modulo G; after the merge every row holds the same totals.
-    float mh[G], lh[G];
+    // h modulo G.  The maxima and normalisers are combined over the rows in
+    // every lane; the N = G * VE rescaled accumulators of a lane are
+    // reduce-scattered: row g ends with the totals of values [g N/4,
+    // (g + 1) N/4), value i standing for head i / VE, slot i % VE.
+    float mh[G], lh[G], fh[G];
     static_for<G>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         mh[h] = group_bcast<G, h>(st.m);
@@ -594,21 +599,40 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const float M = rows_max(mh[h]);
-        const float f = fast_exp2(mh[h] - M);
-        lh[h] = rows_sum(lh[h] * f);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) st.acc[h][e] = rows_sum(st.acc[h][e] * f);
+        fh[h] = fast_exp2(mh[h] - M);
+        lh[h] = rows_sum(lh[h] * fh[h]);
         mh[h] = M;
+    }
+    constexpr int N = G * VE, N2 = N / 2, N4 = N / 4;
+    // A swap of (x, y) hands the upper 32 lanes' x to the lower lanes' y and
+    // the lower lanes' y to the upper lanes' x (likewise odd and even rows for
+    // the 16-lane swap): the lower half keeps the first half of the values,
+    // the upper half the second.
+    float half[N2];
+#pragma unroll
+    for (int j = 0; j < N2; ++j) {
+        const float a = st.acc[j / VE][j % VE] * fh[j / VE];
+        const float z = st.acc[(N2 + j) / VE][(N2 + j) % VE] * fh[(N2 + j) / VE];
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(z),
+                                                        false, false);
+        half[j] = g >= 2 ? z + __uint_as_float(r[0]) : a + __uint_as_float(r[1]);
+    }
+    float quarter[N4];
+#pragma unroll
+    for (int j = 0; j < N4; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(
+            __float_as_uint(half[j]), __float_as_uint(half[N4 + j]), false, false);
+        quarter[j] = (g & 1) ? half[N4 + j] + __uint_as_float(r[0])
+                          : half[j] + __uint_as_float(r[1]);
     }
 
     // ---- merge the waves through LDS ------------------------------------------
     __shared__ float2 sm_ml[NW][G];
     __shared__ float sm_acc[NW][G][D];
-    if (lane < 16) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) sm_acc[wave][h][acc_elem<DT, D>(c16, e)] = st.acc[h][e];
+    for (int j = 0; j < N4; ++j) {
+        const int i = g * N4 + j;
+        sm_acc[wave][i / VE][acc_elem<DT, D>(c16, i % VE)] = quarter[j];
     }
     if (lane == 0) {
 #pragma unroll
