@@ -101,7 +101,7 @@ class Workload:
                                           self.cus) if num_partitions == 0
                   else num_partitions)
         tiles = c.max_blocks * c.block_size // 16   # partitions split 16-token tiles
-        self.P = max(1, min(self.P, tiles))
+        self.P = max(1, min(self.P, tiles, 4096))   # the library's partition limit
         self.num_partitions = num_partitions
         self.lib = pa.load()
 

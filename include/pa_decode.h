@@ -115,7 +115,7 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
 /*
  * pa_decode with the choices exposed.
  *   num_partitions   0 = heuristic (as pa_decode), 1 = single pass, n > 1 =
- *                    P = min(n, T) partitions, split as above.
+ *                    P = min(n, T, 4096) partitions, split as above.
  *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
  *                    treated like -1 instead of being read (a guard against
  *                    out-of-range ids).
@@ -147,8 +147,9 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
  * partition stores
  * (-1e30, 0, zeros).  pa_merge_partials combines them into out.
  * Partitions are split as above; every partition, empty ones included,
- * writes its slot.  num_partitions must be >= 1 and is used as given
- * (P = num_partitions).
+ * writes its slot.  num_partitions must be >= 1 (else PA_ERR_VALUE) and at
+ * most 4096 (else PA_ERR_UNSUPPORTED), and is used as given (P =
+ * num_partitions).
  */
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_tables, const int32_t *context_lens, int B, int H,

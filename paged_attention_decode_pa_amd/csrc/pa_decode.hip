@@ -313,9 +313,9 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         if (cus < 0) return cus;
         P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
     } else {
-        P = clamp_partitions(table_tiles(max_blocks, block_size), num_partitions);
+        P = clamp_partitions(table_tiles(max_blocks, block_size),
+                             num_partitions < kMaxPartitions ? num_partitions : kMaxPartitions);
     }
-    if (P > kMaxPartitions) return PA_ERR_UNSUPPORTED;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
     p.out = out;

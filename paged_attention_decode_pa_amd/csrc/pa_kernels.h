@@ -9,12 +9,14 @@
 // * One workgroup per (kvh, b[, partition]) serves all G = H / Hkv query heads
 //   of the group, so each K/V row is read from HBM once per kv head, not once
 //   per query head.
-// * A wave consumes one 16-token tile per step.  Block ids are read with
-//   scalar loads one group of tiles ahead, so they are wave-uniform and each
-//   tile gets a raw buffer descriptor (SGPRs) over exactly its live rows of
-//   head kvh; the per-lane offsets never change.  Slots past the context and
-//   -1 blocks fall outside the descriptor's range and read as zeros without a
-//   memory access, so the streaming loop has no branches.
+// * A wave consumes one 16-token tile per step; partition p takes a
+//   sequence's tiles p, p + P, ... and its 4 waves every 4th of those.  Block
+//   ids are read with scalar loads one group of tiles ahead, so they are
+//   wave-uniform and each tile gets a raw buffer descriptor (SGPRs) over
+//   exactly its live rows of head kvh; the per-lane offsets never change.
+//   Slots past the context and -1 blocks fall outside the descriptor's range
+//   and read as zeros without a memory access, so the streaming loop has no
+//   branches.
 // * Scores: the 16 tokens x G heads x D product is a small dense contraction,
 //   run on the matrix cores: rows = the tile's 16 tokens, columns = the G
 //   query heads repeated to 16, reduction = head_dim.  Each lane's 16-byte K
@@ -24,13 +26,15 @@
 // * Online softmax per (row g, head): running max m and normaliser l in log2
 //   units (scale * log2 e is folded into one multiply), so each lane updates
 //   its own statistics from its 4 scores with no cross-lane max per tile.  The
-//   max is a reference that moves only when a score exceeds it by more than
-//   2^8 (a wave-wide vote), so most tiles skip the rescale of the state.
+//   max is a reference that moves only when a score exceeds it by more than 8
+//   (log2 units, a wave-wide vote), so most tiles skip the rescale of the
+//   state.
 // * V accumulate on the vector ALUs in fp32: lane (g, c) holds D / 16 elements
 //   of the V rows of tokens 4g..4g+3 and accumulates them for all G heads; the
 //   weights of the other heads come from neighbouring lanes by DPP broadcast.
-// * Epilogue: the 4 row groups of a wave are merged with permlane swaps, the
-//   waves through LDS, always with the rescale-and-sum rule
+// * Epilogue: the 4 row groups of a wave are merged with permlane swaps (the
+//   accumulators reduce-scattered, a quarter to each row), the waves through
+//   LDS, always with the rescale-and-sum rule
 //   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)).  A single
 //   pass writes O / L.  With partitions, each workgroup writes (M, L, O) to
 //   the workspace; then either a separate merge kernel combines them, or (fused

@@ -170,6 +170,19 @@ def test_ex_and_split_half_validation():
         pa.PA_ERR_SHAPE
 
 
+def test_forced_partitions_clamp_rather_than_fail():
+    # more partitions than tiles or than 4096 are clamped: the call passes
+    # validation and only then finds no device here
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    lib = pa.load()
+    args = [FAKE["out"], FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128,
+            16, 8192, 0.088, 1, None]
+    assert lib.pa_decode_ex(*args, 10 ** 6, 0, None, 0) == pa.PA_ERR_DEVICE
+    assert lib.pa_decode_ex(*args, 5000, 0, None, 0) == pa.PA_ERR_DEVICE
+
+
 def test_binding_rejects_bad_tensors():
     import torch
     q = torch.zeros(2, 32, 128, dtype=torch.float16)

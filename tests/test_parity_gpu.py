@@ -225,10 +225,10 @@ def test_empty_batch_launches_nothing(gpu):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("parts", [0, 1, 4096])
+@pytest.mark.parametrize("parts", [0, 1, 4096, 10 ** 6])
 def test_long_context_many_chunks(gpu, dtype, parts):
-    # 131072 tokens = 8192 blocks: a single pass walks 2048 blocks per wave
-    # (32 table chunks of 64); 4096 partitions is the largest count
+    # 131072 tokens = 8192 tiles: a single pass walks 2048 tiles per wave;
+    # 4096 partitions is the largest count (larger requests are clamped to it)
     case = pi.make_case(1, 131072 - 9, 32, 8, 128, 16, dtype=dtype, seed=11, pool=8192)
     say(f"long context {dtype} P={parts}")
     out = run_gpu(case, gpu, num_partitions=parts)
