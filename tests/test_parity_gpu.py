@@ -486,3 +486,55 @@ def test_partials_follow_documented_split(gpu):
     # sequence 0 has 6 tiles (partitions 0-5), sequence 3 has 44 (all 8)
     assert empty[2].all() and (~empty[1, :, 0]).all() and empty[1, :, 1:].all()
     assert (~empty[0, :, :6]).all() and empty[0, :, 6:].all() and (~empty[3]).all()
+
+
+def random_case(seed):
+    """A seeded random draw over the built shape space: dtype, head dim, group
+    size, block size, batch, ragged lengths (zeros included), holes, partitions
+    (0 = heuristic) and which split path runs."""
+    rng = np.random.default_rng(seed)
+    dtype = ["f32", "bf16", "f16"][rng.integers(3)]
+    d = [64, 128, 256][rng.integers(3)]
+    G = [1, 2, 4, 8, 16][rng.integers(5)]
+    if not built(dtype, d, G):
+        G = 2
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    bs = int(2 ** rng.integers(4, 9))
+    B = int(rng.integers(1, 7))
+    max_len = int(rng.choice([40, 300, 3000]))
+    lens = [int(x) for x in rng.integers(0, max_len + 1, size=B)]
+    max_blocks = max(1, max(math.ceil(n / bs) for n in lens)) + int(rng.integers(0, 3))
+    holes = []
+    for b, n in enumerate(lens):
+        nb = math.ceil(n / bs)
+        if nb > 1 and rng.random() < 0.3:
+            holes.append((b, int(rng.integers(nb))))
+    parts = int(rng.choice([0, 0, 1, 2, 3, 7, 33]))
+    two_kernel = bool(rng.random() < 0.25)
+    need = sum(math.ceil(n / bs) for n in lens)
+    case = pi.make_case(B, lens, G * Hkv, Hkv, d, bs, dtype=dtype, seed=seed,
+                        max_blocks=max_blocks, pool=need + 2, holes=holes)
+    return case, parts, two_kernel
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes(gpu, seed):
+    case, parts, two_kernel = random_case(7000 + seed)
+    desc = (f"seed {7000 + seed}: {case.dtype} d={case.head_dim} H={case.num_heads} "
+            f"Hkv={case.num_kv_heads} bs={case.block_size} lens={case.context_lens.tolist()} "
+            f"P={parts} two_kernel={two_kernel}")
+    say(desc)
+    ws = None
+    if two_kernel and parts > 1:
+        tiles = case.max_blocks * case.block_size // 16
+        P = min(parts, tiles)
+        nbytes = pa.pa_workspace_bytes(case.batch, case.num_heads, case.head_dim, P)
+        ws = (torch.empty(max(nbytes, 16), dtype=torch.uint8, device=gpu), nbytes)
+    out = run_gpu(case, gpu, num_partitions=parts, workspace=ws)
+    assert_close(to_f64(out), oracle.decode_case(case), case.dtype, desc)
+    poisoned = pi.poison_unused(case)
+    clean = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    clean.block_tables = poisoned.block_tables
+    a = run_gpu(clean, gpu, num_partitions=parts, workspace=ws)
+    b = run_gpu(poisoned, gpu, num_partitions=parts, workspace=ws)
+    assert torch.equal(a, b), desc
