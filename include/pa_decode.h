@@ -83,12 +83,18 @@ enum {
 
 /*
  * Partitions.  With P partitions, sequence b's n_b = ceil(context_lens[b] / 16)
- * tiles of 16 tokens are dealt out in turn: partition p takes tiles p, p + P,
- * p + 2P, ... below n_b.  The partitions of a sequence so differ by at most
- * one tile whatever its length, and a batch of short contexts in a wide table
- * still keeps every partition busy; when n_b < P the last P - n_b partitions
- * of b are empty.  (The merge is a sum over the partitions' tokens, so they
- * need not be contiguous.)
+ * tiles of 16 tokens go to its first busy_b partitions: the tiles are dealt in
+ * runs of 2 consecutive tiles to the 4 * busy_b lanes (4 per partition) in
+ * turn, partition p owning lanes 4p .. 4p + 3.  So the split follows each
+ * sequence's own length -- a batch of short contexts in a wide table still
+ * keeps its partitions busy -- and the merge is a sum over the partitions'
+ * tokens, which need not be contiguous.  busy_b = min(n_b, P) when the count
+ * is given (pa_decode_ex with num_partitions > 0, pa_decode_partials); with
+ * the heuristic count (pa_decode) a sequence uses only the partitions its
+ * length fills, busy_b = min(P, ceil(n_b / T)), T = 8 tiles while the B * Hkv
+ * (sequence, kv head) units are fewer than the device's compute units and
+ * T = 128 otherwise, so that in a batch that already covers the device only
+ * long sequences split.  Partitions p >= busy_b are empty.
  *
  * One decode step (the signature the docs page's kernel launch wraps:
  * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
@@ -165,10 +171,12 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
 /*
  * The launch heuristic (pure; no HIP call).  Work units are the B * Hkv
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
- * they already cover the device (>= num_cus) it returns 1.  Otherwise it
- * splits each unit's T tiles into enough partitions to give about num_cus
- * workgroups, keeping at least 8 tiles (128 tokens) per partition of a full
- * row.  Returns >= 1 (1 for non-positive inputs or block_size below 16).
+ * they are fewer than num_cus it splits each unit's T tiles into enough
+ * partitions to give about num_cus workgroups, keeping at least 8 tiles (128
+ * tokens) per partition of a full row.  When they already cover the device it
+ * returns ceil(T / 128), at most 8: room for the long sequences of the batch
+ * to split into partitions of about 2048 tokens (see Partitions).  Returns
+ * >= 1 (1 for non-positive inputs or block_size below 16).
  */
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
 

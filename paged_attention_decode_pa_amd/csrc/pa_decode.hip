@@ -19,7 +19,14 @@ namespace {
 using namespace pa_detail;
 
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kMinTilesPerPartition = 8;  // 128 tokens
+constexpr int kMinTilesPerPartitionLog2 = 3;  // 8 tiles, 128 tokens
+constexpr int kMinTilesPerPartition = 1 << kMinTilesPerPartitionLog2;
+// When the (sequence, kv head) units alone cover the device, only sequences
+// much longer than a partition of this many tiles (2048 tokens) split, and
+// into at most kMaxLongSplit partitions: a long sequence in a batch of short
+// ones otherwise sets the pace on its own.
+constexpr int kLongPartitionTilesLog2 = 7;  // 128 tiles
+constexpr int kMaxLongSplit = 8;
 constexpr int kMaxPartitions = 4096;
 
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
@@ -230,6 +237,7 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.max_blocks = max_blocks;
     p.P = P;
     p.tiles_log2 = log2_int(block_size / kTile);
+    p.part_tiles_log2 = 0;  // every partition up to min(n, P) busy
     p.max_tiles = table_tiles(max_blocks, block_size);
     p.qk_scale = scale * kLog2e;
     return p;
@@ -256,9 +264,12 @@ extern "C" {
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {
     if (B <= 0 || Hkv <= 0 || max_blocks <= 0 || block_size < kTile || num_cus <= 0) return 1;
     const long long units = (long long)B * Hkv;
-    if (units >= num_cus) return 1;
     const long long tiles = (long long)max_blocks * block_size / kTile;
     if (tiles > 0x7FFFFFFF) return 1;
+    if (units >= num_cus) {
+        const long long P = (tiles + (1LL << kLongPartitionTilesLog2) - 1) >> kLongPartitionTilesLog2;
+        return P < kMaxLongSplit ? (int)P : kMaxLongSplit;
+    }
     long long P = (num_cus + units - 1) / units;
     const long long cap = tiles / kMinTilesPerPartition;
     if (P > cap) P = cap;
@@ -308,16 +319,25 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     int dev = 0;
     if ((rc = current_device(&dev)) != PA_OK) return rc;
     int P;
+    int part_tiles_log2 = 0;
+    int fused_mode = kFused;
     if (num_partitions == 0) {
         const int cus = device_cus(dev);
         if (cus < 0) return cus;
         P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
+        // a sequence uses the partitions its length fills: at least 8 tiles
+        // each, 128 when the units alone cover the device
+        const bool covered = (long long)B * Hkv >= cus;
+        part_tiles_log2 = covered ? kLongPartitionTilesLog2 : kMinTilesPerPartitionLog2;
+        // with the units covering the device most partitions are empty
+        if (covered) fused_mode = kFusedLate;
     } else {
         P = clamp_partitions(table_tiles(max_blocks, block_size),
                              num_partitions < kMaxPartitions ? num_partitions : kMaxPartitions);
     }
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
+    p.part_tiles_log2 = part_tiles_log2;
     p.out = out;
     if (P == 1) return run_main(p, dtype, d, v.G, kSingle, s);
     const size_t need = workspace_layout(B, H, P, d).total;
@@ -333,7 +353,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     if ((rc = library_buffers(dev, s, need, (size_t)B * Hkv, &ws, &tickets)) != PA_OK) return rc;
     attach_workspace(p, ws, d);
     p.counters = tickets;
-    return run_main(p, dtype, d, v.G, kFused, s);
+    return run_main(p, dtype, d, v.G, fused_mode, s);
 }
 
 int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,

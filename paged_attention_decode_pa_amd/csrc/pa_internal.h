@@ -25,8 +25,11 @@ constexpr int kMaxBlockSize = 256;
 #endif
 constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;  // waves per workgroup
 
-// What a workgroup does with its merged (M, L, O).
-enum Mode { kSingle = 0, kPartials = 1, kFused = 2 };
+// What a workgroup does with its merged (M, L, O).  kFusedLate is kFused
+// with the query loaded only once a partition knows it has tiles: used when
+// most partitions of a launch are empty (units covering the device, long
+// sequences only splitting), so that those leave without loading it.
+enum Mode { kSingle = 0, kPartials = 1, kFused = 2, kFusedLate = 3 };
 
 struct Params {
     const char *q;
@@ -45,6 +48,7 @@ struct Params {
     int b0;               // first sequence of this launch (grid y covers b0 ..)
     int tiles_log2;       // log2(block_size / 16): tiles per physical block
     int max_tiles;        // max_blocks * block_size / 16
+    int part_tiles_log2;  // a sequence of n tiles uses min(P, ceil(n / 2^this)) partitions
     float qk_scale;       // scale * log2(e)
 };
 

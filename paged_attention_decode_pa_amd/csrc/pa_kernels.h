@@ -456,6 +456,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     using Geo = Geometry<DT, D>;
     constexpr int KL = Geo::kKLoads, VE = Geo::kVElems, VW = Geo::kVWords;
     constexpr int VLD = Geo::kVLoads, VWIDTH = Geo::kVWidth;
+    constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate;
 
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
@@ -466,20 +467,18 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const int c16 = lane & 15;  // MFMA column / token of the tile for K
     const int g = lane >> 4;    // MFMA row group: tokens 4g..4g+3 for V
 
-    // Partition p of a sequence takes its tiles p, p + P, p + 2P, ...; wave w
-    // of the partition takes every NW-th of those, starting at the w-th.  For
-    // any context length the partitions differ by at most one tile, and which
-    // tiles a wave owns does not depend on the length, so its first table
+    // Tiles are dealt in runs of DEPTH consecutive tiles (one group) to the
+    // busy * NW (partition, wave) lanes in turn: lane L = part * NW + wave
+    // takes runs L, L + busy * NW, ...  `busy`, the partitions a sequence
+    // uses, follows its length -- ceil(n / 2^part_tiles_log2) of them, at most
+    // P -- but a lane's first run does not depend on it, so its first table
     // entries are fetched before the length has arrived.
-    const int first = part + p.P * wave;  // this wave's tiles: first + stride * i
-    const int stride = p.P * NW;
+    const int first = DEPTH * (part * NW + wave);  // first tile of the lane's first run
     const int32_t *trow = p.table + (long long)b * p.max_blocks;
-    // Table entry of the block holding the wave's i-th tile, the read clamped
-    // into the row so it always stays in bounds (entries past the context are
-    // read, never used).
-    auto tile_of = [&](int i) -> int { return first + stride * i; };
-    auto table_at = [&](int i) -> int {
-        const int e = tile_of(i) >> p.tiles_log2;
+    // Table entry of the block holding tile j, the read clamped into the row so
+    // it always stays in bounds (entries past the context are read, never used).
+    auto table_at = [&](int j) -> int {
+        const int e = j >> p.tiles_log2;
         return trow[e < p.max_blocks ? e : p.max_blocks - 1];
     };
 
@@ -488,26 +487,33 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     int ctx = p.lens[b];
     int raw0[DEPTH];
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) raw0[s] = table_at(s);
+    for (int s = 0; s < DEPTH; ++s) raw0[s] = table_at(first + s);
     // B operand: the query of head kvh*G + c16%G, chunk (4m + g) of 16 bytes.
+    // Loaded here, with the length and table entries, except in kFusedLate
+    // (after the empty partitions have left; loads complete in order, so a
+    // query issued behind the first tiles delays their update a little).
     const char *qrow = p.q + ((long long)b * p.H + kvh * G + (c16 % G)) * Geo::kRowBytes;
     u32x4 qr[KL];
+    auto load_query = [&]() {
 #pragma unroll
-    for (int m = 0; m < KL; ++m) qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
+        for (int m = 0; m < KL; ++m)
+            qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
+    };
+    if constexpr (MODE != kFusedLate) load_query();
 
     ctx = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
     const int ntiles = (int)(((unsigned)ctx + kTile - 1) / kTile);
-    // Partitions holding a tile (the first min(n, P)); the fused merge waits
-    // for exactly these.
-    const int busy = min(ntiles, p.P);
+    // Partitions holding tiles (the first `busy`); the fused merge waits for
+    // exactly these.
+    const int want = (ntiles + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2;
+    const int busy = want < p.P ? want : p.P;
+    const bool idle = part >= busy;             // owns no tile
+    const int stride = busy * NW * DEPTH;       // tiles between a lane's runs
     // One busy partition (or none) writes the output itself, as a single pass;
     // in the fused mode a partition without tiles adds nothing to the merge
     // and writes nothing (partition 0 of an empty sequence writes zeros).
-    // Such a partition still runs the (empty) prologue and epilogue: an early
-    // exit that depends on the context length would let the compiler hold
-    // back the query and table loads until that length has arrived.
-    const bool direct = MODE == kSingle || (MODE == kFused && busy <= 1);
-    const bool silent = MODE == kFused && part >= max(busy, 1);
+    const bool direct = MODE == kSingle || (kFusedMerge && busy <= 1);
+    const bool silent = kFusedMerge && part >= max(busy, 1);
 
     // Per-lane byte offsets inside one tile's rows of head kvh; never change.
     const unsigned koff = c16 * p.tok_bytes + 16 * g;
@@ -528,19 +534,18 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) st.acc[h][e] = 0.f;
 
-    // Live tokens of the wave's i-th tile given its block's table entry: 0 past
-    // the context and for -1 (or out-of-pool) entries.
-    // (Negative ids compare above any pool limit as unsigned.)
-    auto live_tokens = [&](int i, int id) -> int {
-        const int j = tile_of(i);
+    // Live tokens of tile j given its block's table entry: 0 past the context,
+    // for -1 (or out-of-pool) entries and in an idle partition.  (Negative ids
+    // compare above any pool limit as unsigned.)
+    auto live_tokens = [&](int j, int id) -> int {
         const int rem = ctx - j * kTile;
         const int n = rem < kTile ? rem : kTile;
-        return (j < ntiles && (unsigned)id < p.pool_limit) ? n : 0;
+        return (!idle && j < ntiles && (unsigned)id < p.pool_limit) ? n : 0;
     };
-    // Loads of the wave's i-th tile: its rows start at the block's base plus
-    // the tile's place inside the block.
-    auto issue = [&](u32x4 *kd, unsigned (*vd)[VW], int i, int id, int nlive) {
-        const int in_block = tile_of(i) & ((1 << p.tiles_log2) - 1);
+    // Loads of tile j: its rows start at the block's base plus the tile's place
+    // inside the block.
+    auto issue = [&](u32x4 *kd, unsigned (*vd)[VW], int j, int id, int nlive) {
+        const int in_block = j & ((1 << p.tiles_log2) - 1);
         const long long off =
             nlive > 0 ? (long long)id * p.blk_bytes + (long long)in_block * kTile * p.tok_bytes : 0;
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off, nlive * p.tok_bytes);
@@ -554,25 +559,29 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
                 load_words<VWIDTH>(rv, voff[r][s], vd[r] + s * (VWIDTH / 4));
     };
 
-    // DEPTH tiles in flight: slot s of group k holds the wave's tile kDEPTH + s.
-    // The first group is issued and consumed even by a wave with no tile: its
-    // descriptors are empty, so the loads return zeros without a memory access
-    // and the masked update leaves the state as it is.  Doing so keeps every
-    // use of the query and table loads unconditional, so the compiler issues
-    // them together with the context-length load instead of after it.
+    // DEPTH tiles in flight: slot s of group k holds tile first + stride * k + s.
+    // The first group is issued even by a lane with no tile: its descriptors
+    // are empty, so the loads return zeros without a memory access.  Issuing
+    // it before any exit keeps the table loads' uses unconditional, so the
+    // compiler issues them together with the context-length load.
     u32x4 kr[DEPTH][KL];
     unsigned vr[DEPTH][4][VW];
     int nl[DEPTH];
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) {
-        nl[s] = live_tokens(s, raw0[s]);
-        issue(kr[s], vr[s], s, raw0[s], nl[s]);
+        nl[s] = live_tokens(first + s, raw0[s]);
+        issue(kr[s], vr[s], first + s, raw0[s], nl[s]);
     }
+    if constexpr (kFusedMerge) {
+        if (silent) return;  // nothing in flight touches memory
+    }
+    if constexpr (MODE == kFusedLate) load_query();
     int k = 0;
     do {
+        const int nbase = first + stride * (k + 1);  // the next group's first tile
         int nid[DEPTH];
 #pragma unroll
-        for (int s = 0; s < DEPTH; ++s) nid[s] = table_at((k + 1) * DEPTH + s);
+        for (int s = 0; s < DEPTH; ++s) nid[s] = table_at(nbase + s);
         // (each tile's scores right before its update: computing the group's
         // scores first makes the first update wait for the later tiles' K
         // rows as well, since loads complete in order, and measures slower)
@@ -580,13 +589,13 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         for (int s = 0; s < DEPTH; ++s) {
             update_tile<DT, D, G>(st, tile_scores<DT, D>(kr[s], qr), vr[s], p.qk_scale, g,
                                   nl[s]);
-            nl[s] = live_tokens((k + 1) * DEPTH + s, nid[s]);
+            nl[s] = live_tokens(nbase + s, nid[s]);
             // (tiles past the context are issued too, with empty ranges: a
             // branch here measures slower than the loads it would save)
-            issue(kr[s], vr[s], (k + 1) * DEPTH + s, nid[s], nl[s]);
+            issue(kr[s], vr[s], nbase + s, nid[s], nl[s]);
         }
         ++k;
-    } while (tile_of(k * DEPTH) < ntiles);  // group k still holds a live tile
+    } while (!idle && first + stride * k < ntiles);  // group k still holds a live tile
 
     // ---- merge the 4 row groups of the wave -----------------------------------
     // The (m, l) of row g and head h sit in the lanes of row g whose column is
@@ -675,7 +684,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         }
     }
 
-    if constexpr (MODE == kFused) {
+    if constexpr (kFusedMerge) {
         if (direct || silent) return;
         // Publish this partition (its coherent stores complete before the
         // barrier), take a ticket; the last of the `busy` workgroups of
@@ -739,7 +748,8 @@ hipError_t dispatch_mode(const Params &p, int G, int mode, int nseq, hipStream_t
     switch (mode) {
         case kSingle: return dispatch_g<DT, D, kSingle>(p, G, nseq, stream);
         case kPartials: return dispatch_g<DT, D, kPartials>(p, G, nseq, stream);
-        default: return dispatch_g<DT, D, kFused>(p, G, nseq, stream);
+        case kFused: return dispatch_g<DT, D, kFused>(p, G, nseq, stream);
+        default: return dispatch_g<DT, D, kFusedLate>(p, G, nseq, stream);
     }
 }
 

@@ -42,7 +42,10 @@ def test_strerror_covers_codes():
     (16, 8, 16, 16, 256, 2),      # 128 units -> 2 partitions of 8 tiles
     (4, 8, 128, 16, 256, 8),      # 32 units -> 8 partitions of 16 tiles
     (1, 8, 1024, 16, 256, 32),    # 8 units -> 32 partitions of 32 tiles
-    (32, 8, 1024, 16, 256, 1),    # 256 units already fill 256 CUs
+    (32, 8, 1024, 16, 256, 8),    # units fill the CUs: split long rows, 128 tiles each, <= 8
+    (32, 8, 64, 16, 256, 1),      # ... a row of 64 tiles does not split
+    (64, 8, 300, 16, 256, 3),     # ... 300 tiles -> 3
+    (64, 8, 100000, 16, 256, 8),  # ... at most 8
     (1, 1, 100, 16, 256, 12),     # capped at 100 // 8 = 12 (runs of 8 or 9 tiles)
     (1, 8, 7, 16, 256, 1),
     (0, 8, 10, 16, 256, 1),
@@ -63,10 +66,13 @@ def test_choose_partitions_properties():
                 for cus in (80, 256, 304):
                     P = pa.pa_choose_partitions(B, Hkv, mb, 16, cus)
                     assert 1 <= P <= max(1, mb)
-                    if P > 1:
+                    if B * Hkv >= cus:
+                        # units cover the device: only long rows split, into
+                        # partitions of up to 128 tiles, at most 8
+                        assert P == min(8, max(1, math.ceil(mb / 128)))
+                    elif P > 1:
                         # every partition of a full row gets at least 8 tiles
                         assert mb // P >= 8
-                        assert B * Hkv < cus
                         # and about one workgroup per compute unit, not more
                         assert B * Hkv * (P - 1) < cus
 
