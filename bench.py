@@ -58,9 +58,12 @@ def parse():
                     help="CPU work budget of the oracle baseline (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (counter scale)")
-    ap.add_argument("--sweep", action="store_true",
-                    help="instead of the headline: single pass vs split-KV over batch 1 and 4 "
-                         "and KV lengths 512..16384 (the design note's sweep)")
+    ap.add_argument("--sweep", nargs="?", const="design-note", default=None,
+                    choices=["design-note", "ragged", "script", "shapes"],
+                    help="instead of the headline, a sweep: design-note (single pass vs split "
+                         "over batch 1/4 and KV 512..16384), ragged (long-tailed batches), "
+                         "script (the benchmark script's default grid), shapes (the headline "
+                         "problem at other head dims, dtypes and block sizes)")
     return ap.parse_args()
 
 
@@ -264,6 +267,101 @@ SWEEP_KV = (512, 1024, 2048, 4096, 8192, 16384)
 SWEEP_SHAPE = dict(H=32, Hkv=32, d=128, bs=16, dtype="f16")
 
 
+def point(case, dev, steps, warmup, use_graph, parts):
+    """One measured configuration: partition count, µs per step, live GB/s."""
+    import torch
+    w, ts, err = measure(case, dev, steps, warmup, use_graph, parts)
+    row = dict(partitions=w.P, us=round(ts * 1e6, 3), GBps=round(w.bytes / ts / 1e9, 1),
+               max_abs_err=err, algorithmic_bytes=w.bytes)
+    del w
+    torch.cuda.empty_cache()
+    return row
+
+
+def skewed_lens(B, seed):
+    """A long-tailed batch: most lengths uniform in 128..2048, one in ten in
+    8192..16384, the first one 16384."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(128, 2049, size=B)
+    long = rng.random(B) < 0.1
+    lens[long] = rng.integers(8192, 16385, size=int(long.sum()))
+    lens[0] = 16384
+    return [int(x) for x in lens]
+
+
+def sweep_ragged(dev, steps, warmup, use_graph):
+    """Batches of unequal lengths in a table wide enough for the longest
+    (16384 tokens), bf16, 32 query / 8 kv heads, d 128, 16-token blocks; one
+    with -1 holes.  Heuristic partitions against a single pass; GB/s counts
+    live tokens only."""
+    import pa_inputs as pi
+    cases = []
+    for B, seed in ((8, 2), (32, 1), (64, 3)):
+        cases.append((f"B={B} long-tailed", pi.make_case(
+            B, skewed_lens(B, seed), 32, 8, 128, 16, dtype="bf16", seed=seed, max_blocks=1024,
+            name=f"bf16 B={B} long-tailed lengths H=32 Hkv=8 d=128 bs=16 width=1024")))
+    lens = skewed_lens(32, 4)
+    holes = [(b, (n // 16) // 2) for b, n in enumerate(lens) if n >= 64][:16]
+    cases.append(("B=32 long-tailed, 16 holes", pi.make_case(
+        32, lens, 32, 8, 128, 16, dtype="bf16", seed=4, max_blocks=1024, holes=holes,
+        name="bf16 B=32 long-tailed lengths with -1 holes H=32 Hkv=8 d=128 bs=16 width=1024")))
+    cases.append(("B=32 uniform 2048", pi.make_case(
+        32, 2048, 32, 8, 128, 16, dtype="bf16", seed=5, max_blocks=1024,
+        name="bf16 B=32 ctx=2048 H=32 Hkv=8 d=128 bs=16 width=1024")))
+    points = []
+    for label, case in cases:
+        row = dict(case=label, lens_sum=int(case.context_lens.sum()),
+                   lens_max=int(case.context_lens.max()))
+        for tag, parts in (("heuristic", 0), ("single", 1)):
+            r = point(case, dev, steps, warmup, use_graph, parts)
+            row.update({f"{tag}_{k}": v for k, v in r.items() if k != "algorithmic_bytes"})
+            row["algorithmic_bytes"] = r["algorithmic_bytes"]
+        log(f"{label}: heuristic P={row['heuristic_partitions']} {row['heuristic_us']:.1f} us "
+            f"({row['heuristic_GBps']:.0f} GB/s), single {row['single_us']:.1f} us")
+        points.append(row)
+    return dict(metric="decode step us and live-token GB/s, batches of unequal lengths",
+                unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
+                dtype="bf16", data="synthetic", points=points)
+
+
+def sweep_script(dev, steps, warmup, use_graph):
+    """benchmark_decoding.py's default grid: batch 1/8/32 x sequence length
+    128/512/2048, 16 query / 8 kv heads, d 128, block size 256, fp16, a
+    scattered table over a pool of exactly the blocks needed."""
+    import pa_inputs as pi
+    points = []
+    for B in (1, 8, 32):
+        for seq in (128, 512, 2048):
+            case = pi.make_case(B, seq, 16, 8, 128, 256, dtype="f16", seed=B * 10000 + seq,
+                                name=f"f16 B={B} ctx={seq} H=16 Hkv=8 d=128 bs=256")
+            r = point(case, dev, steps, warmup, use_graph, 0)
+            log(f"script grid B={B} seq={seq}: P={r['partitions']} {r['us']:.2f} us "
+                f"({r['GBps']:.0f} GB/s)")
+            points.append(dict(batch=B, seq_len=seq, **r))
+    return dict(metric="decode step us and GB/s, the benchmark script's default grid",
+                unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
+                dtype="f16", data="synthetic", points=points)
+
+
+def sweep_shapes(dev, steps, warmup, use_graph):
+    """The headline problem (B=1, 16384 tokens, 32 query / 8 kv heads) at the
+    other built head dims, element types and block sizes."""
+    import pa_inputs as pi
+    points = []
+    for dtype, d, bs in (("bf16", 128, 16), ("bf16", 64, 16), ("bf16", 256, 16),
+                         ("f16", 128, 16), ("f32", 128, 16), ("bf16", 128, 256),
+                         ("f16", 256, 256)):
+        case = pi.make_case(1, 16384, 32, 8, d, bs, dtype=dtype, seed=d + bs,
+                            pool=2 * 16384 // bs,
+                            name=f"{dtype} B=1 ctx=16384 H=32 Hkv=8 d={d} bs={bs}")
+        r = point(case, dev, steps, warmup, use_graph, 0)
+        log(f"{case.name}: P={r['partitions']} {r['us']:.2f} us ({r['GBps']:.0f} GB/s)")
+        points.append(dict(dtype=dtype, head_dim=d, block_size=bs, **r))
+    return dict(metric="decode step us and GB/s at other shapes of the headline problem",
+                unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
+                data="synthetic", points=points)
+
+
 def sweep(dev, steps, warmup, use_graph):
     import torch
     import pa_inputs as pi
@@ -319,7 +417,9 @@ def main():
     dev = torch.device("cuda:0")
     use_graph = not args.eager
     if args.sweep:
-        print(json.dumps(sweep(dev, min(args.steps, 500), args.warmup, use_graph)), flush=True)
+        fn = {"design-note": sweep, "ragged": sweep_ragged, "script": sweep_script,
+              "shapes": sweep_shapes}[args.sweep]
+        print(json.dumps(fn(dev, min(args.steps, 500), args.warmup, use_graph)), flush=True)
         return
 
     per_config = []
