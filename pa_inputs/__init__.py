@@ -54,11 +54,17 @@ def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     round to +-inf as IEEE RNE prescribes.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    # In 32-bit arithmetic: for every finite value and +-inf, u + 0x7FFF + lsb
+    # stays below 2^32 (the largest, -FLT_MAX = 0xFF7FFFFF, reaches 0xFF807FFF);
+    # NaNs are replaced below.
+    u = x.view(np.uint32)
+    t = (u >> 16) & 1
+    t += u
+    t += 0x7FFF
+    t >>= 16
+    rounded = t.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        rounded = rounded.copy()
         rounded[nan] = BF16_NAN_BITS
     return rounded
 
@@ -228,11 +234,12 @@ def make_case(
     else:
         raise ValueError(f"unknown table kind {table!r}")
 
+    # sequence b takes the next need[b] entries of `order`, in sequence order
     tables = np.full((B, max_blocks), -1, dtype=np.int32)
-    pos = 0
-    for b in range(B):
-        tables[b, :need[b]] = order[pos:pos + need[b]]
-        pos += need[b]
+    counts = np.asarray(need, dtype=np.int64)
+    rows = np.repeat(np.arange(B), counts)
+    cols = np.arange(total) - np.repeat(np.cumsum(counts) - counts, counts)
+    tables[rows, cols] = order[:total]
     for (b, j) in holes or ():
         tables[b, j] = -1
 

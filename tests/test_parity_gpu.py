@@ -543,3 +543,25 @@ def test_random_shapes(gpu, seed):
     a = run_gpu(clean, gpu, num_partitions=parts, workspace=ws)
     b = run_gpu(poisoned, gpu, num_partitions=parts, workspace=ws)
     assert torch.equal(a, b), desc
+
+
+@pytest.mark.parametrize("parts", [0, 1, 2])
+def test_batch_beyond_one_launch(gpu, parts):
+    # more sequences than one launch's grid holds (65535): the library issues
+    # several launches; fused tickets are indexed by the global sequence
+    B = 65600
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(0, 17, size=B)]
+    case = pi.make_case(B, lens, 2, 1, 64, 16, dtype="bf16", seed=12, max_blocks=2)
+    say(f"B={B} tiny contexts P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"B={B} P={parts}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_many_kv_heads(gpu, dtype):
+    case = pi.make_case(3, [700, 5, 129], 64, 64, 128, 32, dtype=dtype, seed=13, pool=40)
+    for parts in (0, 1, 3):
+        say(f"Hkv=64 {dtype} P={parts}")
+        out = run_gpu(case, gpu, num_partitions=parts)
+        assert_close(to_f64(out), oracle.decode_case(case), dtype, f"Hkv=64 P={parts}")
