@@ -565,3 +565,23 @@ def test_many_kv_heads(gpu, dtype):
         say(f"Hkv=64 {dtype} P={parts}")
         out = run_gpu(case, gpu, num_partitions=parts)
         assert_close(to_f64(out), oracle.decode_case(case), dtype, f"Hkv=64 P={parts}")
+
+
+@pytest.mark.parametrize("parts", [0, 1, 4])
+def test_context_lens_are_clamped(gpu, parts):
+    # a length beyond max_blocks * block_size counts as the full row and a
+    # negative one as empty (reading R3): the result equals the oracle on the
+    # clamped lengths
+    case = pi.make_case(3, [64, 64, 30], 32, 8, 128, 16, dtype="bf16", seed=14, max_blocks=4,
+                        pool=12)
+    dev_case = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    dev_case.context_lens = np.array([64 + 1000, -5, 30], dtype=np.int32)
+    d = DeviceCase(dev_case, gpu)
+    out = torch.empty_like(d.q)
+    say(f"clamped context lengths P={parts}")
+    pa.pa_decode_ex(out, *d.args(), None, parts, case.num_pool_blocks, None, 0)
+    torch.cuda.synchronize()
+    ref_case = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    ref_case.context_lens = np.array([64, 0, 30], dtype=np.int32)
+    assert_close(to_f64(out), oracle.decode_case(ref_case), "bf16", f"clamp P={parts}")
+    assert (out[1].float() == 0).all()
