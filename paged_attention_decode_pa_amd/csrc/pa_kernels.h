@@ -18,11 +18,14 @@
 //   and read as zeros without a memory access, so the streaming loop has no
 //   branches.
 // * Scores: the 16 tokens x G heads x D product is a small dense contraction,
-//   run on the matrix cores: rows = the tile's 16 tokens, columns = the G
-//   query heads repeated to 16, reduction = head_dim.  Each lane's 16-byte K
-//   load is exactly its MFMA A operand, so no cross-lane reduction is needed
-//   for q.K.  After the MFMAs lane (row g = lane/16, column c = lane%16) holds
-//   the scores of tokens 4g..4g+3 for head c % G.
+//   run on the matrix cores.  Each lane's 16-byte K load is its MFMA A
+//   operand.  In the column layout the rows are the tile's 16 tokens, the
+//   columns the G query heads repeated to 16, and the reduction the head dim,
+//   so no cross-lane reduction is needed; lane (row g = lane/16, column
+//   c = lane%16) ends with the scores of tokens 4g..4g+3 for head c % G.  In
+//   the row layout (16-bit elements, D = 128, G <= 4) each MFMA takes whole
+//   rows of 4 tokens, so K loads cover whole cache lines; two DPP adds sum
+//   the row quarters, and lane (g, c) ends with tokens g, g+4, g+8, g+12.
 // * Online softmax per (row g, head): running max m and normaliser l in log2
 //   units (scale * log2 e is folded into one multiply), so each lane updates
 //   its own statistics from its 4 scores with no cross-lane max per tile.  The
@@ -30,7 +33,7 @@
 //   (log2 units, a wave-wide vote), so most tiles skip the rescale of the
 //   state.
 // * V accumulate on the vector ALUs in fp32: lane (g, c) holds D / 16 elements
-//   of the V rows of tokens 4g..4g+3 and accumulates them for all G heads; the
+//   of the V rows of its 4 tokens and accumulates them for all G heads; the
 //   weights of the other heads come from neighbouring lanes by DPP broadcast.
 // * Epilogue: the 4 row groups of a wave are merged with permlane swaps (the
 //   accumulators reduce-scattered, a quarter to each row), the waves through
@@ -82,7 +85,8 @@ template <> struct ElemBytes<PA_DTYPE_BF16> { static constexpr int value = 2; };
 template <> struct ElemBytes<PA_DTYPE_F16> { static constexpr int value = 2; };
 
 // Load geometry of one 16-token tile for element type DT and head dim D.
-// Lane (g = lane / 16, c16 = lane % 16):
+// Lane (g = lane / 16, c16 = lane % 16), column layout (k_rows_layout below
+// for the other):
 //  * K: token c16's 16-byte chunks 4m + g, m < kKLoads -- exactly the MFMA A
 //    operand of reduction step m (the query's B operand uses the same chunks);
 //  * V: kVElems = D / 16 elements of each of tokens 4g..4g+3, read as kVLoads
@@ -102,6 +106,23 @@ struct Geometry {
     static_assert(kKLoads >= 1 && kRowBytes % 64 == 0, "head dim too small for the K layout");
     static_assert(kVWidth == 8 || kVWidth == 16, "V loads are 8 or 16 bytes");
 };
+
+#ifndef PA_K_ROWS
+#define PA_K_ROWS 1
+#endif
+// Which K layout a kernel reads.  The column layout above hands each MFMA
+// step 64 bytes of each of the tile's 16 rows, so every K load instruction
+// touches 16 half cache lines; the row layout instead gives MFMA step j the
+// whole rows of tokens 4j..4j+3 (A row 4t + a = quarter a of token 4j + t,
+// B column 4b + hh = quarter b of the query of head hh % G), so a K load
+// covers whole lines like a V load, and the quarters' partial dot products
+// are summed across lanes afterwards.  It needs four 64-byte quarters per row
+// and the G heads times 4 quarters to fit the 16 columns: 16-bit elements,
+// D = 128, G <= 4.
+template <int DT, int D, int G>
+constexpr bool k_rows_layout() {
+    return PA_K_ROWS && DT != PA_DTYPE_F32 && D == 128 && G <= 4;
+}
 
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
@@ -205,9 +226,43 @@ __device__ __forceinline__ f32x4 tile_scores(const u32x4 *kr, const u32x4 *qr) {
     return c;
 }
 
+// Row-layout scores (k_rows_layout): step j's MFMA leaves in lane (g, c16),
+// register i, the product of quarter i of token 4j + g with quarter c16 / 4
+// of the query; the diagonal register i = c16 / 4 is that quarter's partial
+// dot product, and the sum over the four quarters -- the lanes c16 mod 4 of
+// the 16-lane row, reached by rotations by 8 and 4 -- is the score.  Each sum
+// adds the same pairs in every lane, so all four lanes hold the same bits.
+// Returns the scores of tokens 4j + g, j = 0..3, for head c16 % G.
+template <int DT>
+__device__ __forceinline__ f32x4 tile_scores_rows(const u32x4 *kr, u32x4 qr, int quarter) {
+    f32x4 s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 c;
+        if constexpr (DT == PA_DTYPE_BF16)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[j]),
+                                                         __builtin_bit_cast(bf16x8, qr), zero,
+                                                         0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[j]),
+                                                        __builtin_bit_cast(f16x8, qr), zero,
+                                                        0, 0, 0);
+        float x = (quarter & 2) ? ((quarter & 1) ? c[3] : c[2]) : ((quarter & 1) ? c[1] : c[0]);
+        // row_ror:8 then row_ror:4 (DPP controls 0x128, 0x124)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF,
+                                                        false));
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF,
+                                                        false));
+        s[j] = x;
+    }
+    return s;
+}
+
 // The softmax update and V accumulation of one tile given its raw scores c
-// (tile_scores).
-template <int DT, int D, int G>
+// (tile_scores or tile_scores_rows: slot r holds token 4g + r, or 4r + g in
+// the row layout, whose V rows vw[r] are).
+template <int DT, int D, int G, bool ROWS>
 __device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
                                             const unsigned (*vw)[Geometry<DT, D>::kVWords],
                                             float qk_scale, int g, int nlive) {
@@ -215,7 +270,8 @@ __device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
     constexpr int VE = Geo::kVElems;
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (4 * g + r < nlive) ? c[r] * qk_scale : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+        s[r] = ((ROWS ? 4 * r + g : 4 * g + r) < nlive) ? c[r] * qk_scale : -INFINITY;
     const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     // The reference max m only moves (and l, acc are rescaled by 2^(m - m'))
     // when some lane of the wave sees a score more than kRescaleSlack above
@@ -457,6 +513,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr int KL = Geo::kKLoads, VE = Geo::kVElems, VW = Geo::kVWords;
     constexpr int VLD = Geo::kVLoads, VWIDTH = Geo::kVWidth;
     constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate;
+    constexpr bool kRows = k_rows_layout<DT, D, G>();
+    constexpr int QL = kRows ? 1 : KL;  // query registers (16 bytes each)
 
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
@@ -465,7 +523,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
     const int lane = threadIdx.x % kWave;
     const int c16 = lane & 15;  // MFMA column / token of the tile for K
-    const int g = lane >> 4;    // MFMA row group: tokens 4g..4g+3 for V
+    const int g = lane >> 4;    // MFMA row group (its tokens: 4g..4g+3, or g + 4r)
 
     // Tiles are dealt in runs of DEPTH consecutive tiles (one group) to the
     // busy * NW (partition, wave) lanes in turn: lane L = part * NW + wave
@@ -493,11 +551,13 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // (after the empty partitions have left; loads complete in order, so a
     // query issued behind the first tiles delays their update a little).
     const char *qrow = p.q + ((long long)b * p.H + kvh * G + (c16 % G)) * Geo::kRowBytes;
-    u32x4 qr[KL];
+    // (row layout: chunk (4 (c16 / 4) + g), quarter c16 / 4 of the row)
+    u32x4 qr[QL];
     auto load_query = [&]() {
 #pragma unroll
-        for (int m = 0; m < KL; ++m)
-            qr[m] = *reinterpret_cast<const u32x4 *>(qrow + 64 * m + 16 * g);
+        for (int m = 0; m < QL; ++m)
+            qr[m] = *reinterpret_cast<const u32x4 *>(
+                qrow + (kRows ? 64 * (c16 >> 2) : 64 * m) + 16 * g);
     };
     if constexpr (MODE != kFusedLate) load_query();
 
@@ -516,13 +576,24 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const bool silent = kFusedMerge && part >= max(busy, 1);
 
     // Per-lane byte offsets inside one tile's rows of head kvh; never change.
-    const unsigned koff = c16 * p.tok_bytes + 16 * g;
+    // Column layout: K chunk 4m + g of token c16, V of tokens 4g + r.  Row
+    // layout: K quarter c16 % 4 (chunk g of it) of token 4m + c16 / 4, V of
+    // tokens 4r + g.
+    unsigned koff[kRows ? KL : 1];
+    if constexpr (kRows) {
+#pragma unroll
+        for (int m = 0; m < KL; ++m)
+            koff[m] = (4 * m + (c16 >> 2)) * p.tok_bytes + 64 * (c16 & 3) + 16 * g;
+    } else {
+        koff[0] = c16 * p.tok_bytes + 16 * g;
+    }
     unsigned voff[4][VLD];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int s = 0; s < VLD; ++s)
-            voff[r][s] = (4 * g + r) * p.tok_bytes + VWIDTH * c16 + 16 * VWIDTH * s;
+            voff[r][s] = (kRows ? 4 * r + g : 4 * g + r) * p.tok_bytes + VWIDTH * c16 +
+                         16 * VWIDTH * s;
     const char *kbase = p.k + kvh * Geo::kRowBytes;
     const char *vbase = p.v + kvh * Geo::kRowBytes;
 
@@ -551,7 +622,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + off, nlive * p.tok_bytes);
         const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + off, nlive * p.tok_bytes);
 #pragma unroll
-        for (int m = 0; m < KL; ++m) kd[m] = load16(rk, koff + 64 * m);
+        for (int m = 0; m < KL; ++m) kd[m] = load16(rk, kRows ? koff[m] : koff[0] + 64 * m);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -587,8 +658,12 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         // rows as well, since loads complete in order, and measures slower)
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-            update_tile<DT, D, G>(st, tile_scores<DT, D>(kr[s], qr), vr[s], p.qk_scale, g,
-                                  nl[s]);
+            if constexpr (kRows)
+                update_tile<DT, D, G, true>(st, tile_scores_rows<DT>(kr[s], qr[0], c16 >> 2),
+                                            vr[s], p.qk_scale, g, nl[s]);
+            else
+                update_tile<DT, D, G, false>(st, tile_scores<DT, D>(kr[s], qr), vr[s],
+                                             p.qk_scale, g, nl[s]);
             nl[s] = live_tokens(nbase + s, nid[s]);
             // (tiles past the context are issued too, with empty ranges: a
             // branch here measures slower than the loads it would save)
