@@ -92,9 +92,11 @@ enum {
  * is given (pa_decode_ex with num_partitions > 0, pa_decode_partials); with
  * the heuristic count (pa_decode) a sequence uses only the partitions its
  * length fills, busy_b = min(P, ceil(n_b / T)), T = 8 tiles while the B * Hkv
- * (sequence, kv head) units are fewer than the device's compute units and
- * T = 128 otherwise, so that in a batch that already covers the device only
- * long sequences split.  Partitions p >= busy_b are empty.
+ * (sequence, kv head) units are fewer than the device's compute units (and
+ * busy_b = 1 for n_b <= 16: one workgroup reads 16 tiles in two rounds of
+ * loads, faster than a split and its merge) and T = 128 otherwise, so that in
+ * a batch that already covers the device only long sequences split.
+ * Partitions p >= busy_b are empty.
  *
  * One decode step (the signature the docs page's kernel launch wraps:
  * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
@@ -173,7 +175,8 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
  * they are fewer than num_cus it splits each unit's T tiles into enough
  * partitions to give about num_cus workgroups, keeping at least 8 tiles (128
- * tokens) per partition of a full row.  When they already cover the device it
+ * tokens) per partition of a full row; a row of at most 16 tiles (256
+ * tokens) does not split.  When they already cover the device it
  * returns ceil(T / 128), at most 8: room for the long sequences of the batch
  * to split into partitions of about 2048 tokens (see Partitions).  Returns
  * >= 1 (1 for non-positive inputs or block_size below 16).

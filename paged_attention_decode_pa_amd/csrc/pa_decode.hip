@@ -27,6 +27,11 @@ constexpr int kMinTilesPerPartition = 1 << kMinTilesPerPartitionLog2;
 // ones otherwise sets the pace on its own.
 constexpr int kLongPartitionTilesLog2 = 7;  // 128 tiles
 constexpr int kMaxLongSplit = 8;
+// A sequence of at most this many tiles is read by one workgroup in two rounds
+// of loads (4 waves x 2 tiles); splitting it saves at most one round trip,
+// less than the split's store-ticket-reload chain costs, so the heuristic
+// leaves it whole.
+constexpr int kUnsplitMaxTiles = 16;
 constexpr int kMaxPartitions = 4096;
 
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
@@ -238,6 +243,7 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.P = P;
     p.tiles_log2 = log2_int(block_size / kTile);
     p.part_tiles_log2 = 0;  // every partition up to min(n, P) busy
+    p.solo_tiles = 0;
     p.max_tiles = table_tiles(max_blocks, block_size);
     p.qk_scale = scale * kLog2e;
     return p;
@@ -270,6 +276,7 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
         const long long P = (tiles + (1LL << kLongPartitionTilesLog2) - 1) >> kLongPartitionTilesLog2;
         return P < kMaxLongSplit ? (int)P : kMaxLongSplit;
     }
+    if (tiles <= kUnsplitMaxTiles) return 1;
     long long P = (num_cus + units - 1) / units;
     const long long cap = tiles / kMinTilesPerPartition;
     if (P > cap) P = cap;
@@ -319,16 +326,18 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     int dev = 0;
     if ((rc = current_device(&dev)) != PA_OK) return rc;
     int P;
-    int part_tiles_log2 = 0;
+    int part_tiles_log2 = 0, solo_tiles = 0;
     int fused_mode = kFused;
     if (num_partitions == 0) {
         const int cus = device_cus(dev);
         if (cus < 0) return cus;
         P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
         // a sequence uses the partitions its length fills: at least 8 tiles
-        // each, 128 when the units alone cover the device
+        // each (none of 16 tiles or fewer splits), 128 when the units alone
+        // cover the device
         const bool covered = (long long)B * Hkv >= cus;
         part_tiles_log2 = covered ? kLongPartitionTilesLog2 : kMinTilesPerPartitionLog2;
+        solo_tiles = covered ? 0 : kUnsplitMaxTiles;
         // with the units covering the device most partitions are empty
         if (covered) fused_mode = kFusedLate;
     } else {
@@ -338,6 +347,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
     p.part_tiles_log2 = part_tiles_log2;
+    p.solo_tiles = solo_tiles;
     p.out = out;
     if (P == 1) return run_main(p, dtype, d, v.G, kSingle, s);
     const size_t need = workspace_layout(B, H, P, d).total;

@@ -48,7 +48,8 @@ struct Params {
     int b0;               // first sequence of this launch (grid y covers b0 ..)
     int tiles_log2;       // log2(block_size / 16): tiles per physical block
     int max_tiles;        // max_blocks * block_size / 16
-    int part_tiles_log2;  // a sequence of n tiles uses min(P, ceil(n / 2^this)) partitions
+    int part_tiles_log2;  // a sequence of n tiles uses min(P, ceil(n / 2^this)) partitions,
+    int solo_tiles;       // or one when n <= solo_tiles
     float qk_scale;       // scale * log2(e)
 };
 

@@ -112,16 +112,27 @@ struct Geometry {
 #endif
 // Which K layout a kernel reads.  The column layout above hands each MFMA
 // step 64 bytes of each of the tile's 16 rows, so every K load instruction
-// touches 16 half cache lines; the row layout instead gives MFMA step j the
-// whole rows of tokens 4j..4j+3 (A row 4t + a = quarter a of token 4j + t,
-// B column 4b + hh = quarter b of the query of head hh % G), so a K load
-// covers whole lines like a V load, and the quarters' partial dot products
-// are summed across lanes afterwards.  It needs four 64-byte quarters per row
-// and the G heads times 4 quarters to fit the 16 columns: 16-bit elements,
-// D = 128, G <= 4.
+// touches 16 half cache lines.  The row layout instead cuts each row into
+// Q = D * 2 / 64 parts of 64 bytes (16-bit elements) and gives MFMA step j
+// the whole rows of T = 16 / Q tokens: A row Q t + a is part a of token
+// T j + t, B column T b + hh is part b of the query of head hh % G.  A K load
+// then covers whole cache lines like a V load, and the parts' partial dot
+// products are summed across lanes afterwards.  The G heads times Q parts
+// must fit the 16 columns, and a lane's useful products must fall in its own
+// row of 16 lanes: 16-bit elements with D = 128 (Q = 4, G <= 4) or D = 64
+// (Q = 2, G <= 8).
 template <int DT, int D, int G>
 constexpr bool k_rows_layout() {
-    return PA_K_ROWS && DT != PA_DTYPE_F32 && D == 128 && G <= 4;
+    return PA_K_ROWS && DT != PA_DTYPE_F32 && ((D == 128 && G <= 4) || (D == 64 && G <= 8));
+}
+
+// Token of slot r (0..3) of the lanes in MFMA row group g: the scores and V
+// rows a lane holds for one tile.
+template <int D, bool ROWS>
+__device__ __forceinline__ int slot_token(int g, int r) {
+    if constexpr (!ROWS) return 4 * g + r;
+    else if constexpr (D == 128) return 4 * r + g;
+    else return 8 * (r >> 1) + 2 * g + (r & 1);
 }
 
 template <typename F, int... I>
@@ -226,42 +237,61 @@ __device__ __forceinline__ f32x4 tile_scores(const u32x4 *kr, const u32x4 *qr) {
     return c;
 }
 
-// Row-layout scores (k_rows_layout): step j's MFMA leaves in lane (g, c16),
-// register i, the product of quarter i of token 4j + g with quarter c16 / 4
-// of the query; the diagonal register i = c16 / 4 is that quarter's partial
-// dot product, and the sum over the four quarters -- the lanes c16 mod 4 of
-// the 16-lane row, reached by rotations by 8 and 4 -- is the score.  Each sum
-// adds the same pairs in every lane, so all four lanes hold the same bits.
-// Returns the scores of tokens 4j + g, j = 0..3, for head c16 % G.
+// x plus its value in the lane N places along this lane's row of 16 (DPP
+// row_ror:N, N = 4 or 8).
+template <int N>
+__device__ __forceinline__ float add_row_ror(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF,
+                                                          0xF, false));
+}
+
 template <int DT>
-__device__ __forceinline__ f32x4 tile_scores_rows(const u32x4 *kr, u32x4 qr, int quarter) {
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == PA_DTYPE_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), zero, 0, 0,
+                                                       0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), zero, 0, 0, 0);
+}
+
+// Row-layout scores (k_rows_layout), slot r for token slot_token<D, true>(g, r),
+// head c16 % G; `part` = c16 / T, the query part of this lane's column.  Step
+// j's MFMA leaves in lane (g, c16), register i, the product of row 4g + i
+// (part (4g + i) % Q of a token) with query part `part`; the registers whose
+// parts match are that part's partial dot products, and the sum over the Q
+// parts -- lanes T apart in the row of 16, reached by DPP rotations -- is the
+// score.  Each sum adds the same pairs in every lane, so all Q lanes hold the
+// same bits.
+//  * D = 128 (Q = 4, T = 4): register `part` holds token 4j + g.
+//  * D = 64 (Q = 2, T = 8): registers `part` and `part` + 2 hold tokens
+//    8j + 2g and 8j + 2g + 1.
+template <int DT, int D>
+__device__ __forceinline__ f32x4 tile_scores_rows(const u32x4 *kr, u32x4 qr, int part) {
     f32x4 s;
+    if constexpr (D == 128) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 c;
-        if constexpr (DT == PA_DTYPE_BF16)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[j]),
-                                                         __builtin_bit_cast(bf16x8, qr), zero,
-                                                         0, 0, 0);
-        else
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kr[j]),
-                                                        __builtin_bit_cast(f16x8, qr), zero,
-                                                        0, 0, 0);
-        float x = (quarter & 2) ? ((quarter & 1) ? c[3] : c[2]) : ((quarter & 1) ? c[1] : c[0]);
-        // row_ror:8 then row_ror:4 (DPP controls 0x128, 0x124)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF,
-                                                        false));
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF,
-                                                        false));
-        s[j] = x;
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 c = mfma_16x16x32<DT>(kr[j], qr);
+            const float x = (part & 2) ? ((part & 1) ? c[3] : c[2]) : ((part & 1) ? c[1] : c[0]);
+            s[j] = add_row_ror<4>(add_row_ror<8>(x));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 c = mfma_16x16x32<DT>(kr[j], qr);
+            s[2 * j] = add_row_ror<8>(part ? c[1] : c[0]);
+            s[2 * j + 1] = add_row_ror<8>(part ? c[3] : c[2]);
+        }
     }
     return s;
 }
 
 // The softmax update and V accumulation of one tile given its raw scores c
-// (tile_scores or tile_scores_rows: slot r holds token 4g + r, or 4r + g in
-// the row layout, whose V rows vw[r] are).
+// (tile_scores or tile_scores_rows): slot r holds token slot_token<D, ROWS>(g,
+// r), whose V row vw[r] is.
 template <int DT, int D, int G, bool ROWS>
 __device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
                                             const unsigned (*vw)[Geometry<DT, D>::kVWords],
@@ -271,7 +301,7 @@ __device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-        s[r] = ((ROWS ? 4 * r + g : 4 * g + r) < nlive) ? c[r] * qk_scale : -INFINITY;
+        s[r] = (slot_token<D, ROWS>(g, r) < nlive) ? c[r] * qk_scale : -INFINITY;
     const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     // The reference max m only moves (and l, acc are rescaled by 2^(m - m'))
     // when some lane of the wave sees a score more than kRescaleSlack above
@@ -515,6 +545,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate;
     constexpr bool kRows = k_rows_layout<DT, D, G>();
     constexpr int QL = kRows ? 1 : KL;  // query registers (16 bytes each)
+    constexpr int kRowsQ = KL, kRowsT = 16 / KL;  // row layout: parts per row, tokens per step
 
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
@@ -529,8 +560,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // busy * NW (partition, wave) lanes in turn: lane L = part * NW + wave
     // takes runs L, L + busy * NW, ...  `busy`, the partitions a sequence
     // uses, follows its length -- ceil(n / 2^part_tiles_log2) of them, at most
-    // P -- but a lane's first run does not depend on it, so its first table
-    // entries are fetched before the length has arrived.
+    // P, or one if n <= solo_tiles -- but a lane's first run does not depend
+    // on it, so its first table entries are fetched before the length has
+    // arrived.
     const int first = DEPTH * (part * NW + wave);  // first tile of the lane's first run
     const int32_t *trow = p.table + (long long)b * p.max_blocks;
     // Table entry of the block holding tile j, the read clamped into the row so
@@ -551,13 +583,14 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // (after the empty partitions have left; loads complete in order, so a
     // query issued behind the first tiles delays their update a little).
     const char *qrow = p.q + ((long long)b * p.H + kvh * G + (c16 % G)) * Geo::kRowBytes;
-    // (row layout: chunk (4 (c16 / 4) + g), quarter c16 / 4 of the row)
+    // (row layout: chunk g of part c16 / T of the row, T = 16 / Q tokens per
+    // MFMA step)
     u32x4 qr[QL];
     auto load_query = [&]() {
 #pragma unroll
         for (int m = 0; m < QL; ++m)
             qr[m] = *reinterpret_cast<const u32x4 *>(
-                qrow + (kRows ? 64 * (c16 >> 2) : 64 * m) + 16 * g);
+                qrow + (kRows ? 64 * (c16 / kRowsT) : 64 * m) + 16 * g);
     };
     if constexpr (MODE != kFusedLate) load_query();
 
@@ -565,7 +598,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const int ntiles = (int)(((unsigned)ctx + kTile - 1) / kTile);
     // Partitions holding tiles (the first `busy`); the fused merge waits for
     // exactly these.
-    const int want = (ntiles + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2;
+    const int want = ntiles > p.solo_tiles
+                         ? (ntiles + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2
+                         : (ntiles > 0 ? 1 : 0);
     const int busy = want < p.P ? want : p.P;
     const bool idle = part >= busy;             // owns no tile
     const int stride = busy * NW * DEPTH;       // tiles between a lane's runs
@@ -576,14 +611,14 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const bool silent = kFusedMerge && part >= max(busy, 1);
 
     // Per-lane byte offsets inside one tile's rows of head kvh; never change.
-    // Column layout: K chunk 4m + g of token c16, V of tokens 4g + r.  Row
-    // layout: K quarter c16 % 4 (chunk g of it) of token 4m + c16 / 4, V of
-    // tokens 4r + g.
+    // Column layout: K chunk 4m + g of token c16.  Row layout: K part
+    // c16 % Q (chunk g of it) of token T m + c16 / Q.  V rows of the slots'
+    // tokens (slot_token).
     unsigned koff[kRows ? KL : 1];
     if constexpr (kRows) {
 #pragma unroll
         for (int m = 0; m < KL; ++m)
-            koff[m] = (4 * m + (c16 >> 2)) * p.tok_bytes + 64 * (c16 & 3) + 16 * g;
+            koff[m] = (kRowsT * m + c16 / kRowsQ) * p.tok_bytes + 64 * (c16 % kRowsQ) + 16 * g;
     } else {
         koff[0] = c16 * p.tok_bytes + 16 * g;
     }
@@ -592,7 +627,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int s = 0; s < VLD; ++s)
-            voff[r][s] = (kRows ? 4 * r + g : 4 * g + r) * p.tok_bytes + VWIDTH * c16 +
+            voff[r][s] = slot_token<D, kRows>(g, r) * p.tok_bytes + VWIDTH * c16 +
                          16 * VWIDTH * s;
     const char *kbase = p.k + kvh * Geo::kRowBytes;
     const char *vbase = p.v + kvh * Geo::kRowBytes;
@@ -659,7 +694,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
             if constexpr (kRows)
-                update_tile<DT, D, G, true>(st, tile_scores_rows<DT>(kr[s], qr[0], c16 >> 2),
+                update_tile<DT, D, G, true>(st,
+                                            tile_scores_rows<DT, D>(kr[s], qr[0], c16 / kRowsT),
                                             vr[s], p.qk_scale, g, nl[s]);
             else
                 update_tile<DT, D, G, false>(st, tile_scores<DT, D>(kr[s], qr), vr[s],

@@ -39,7 +39,8 @@ def test_strerror_covers_codes():
 @pytest.mark.parametrize("B,Hkv,max_blocks,bs,cus,expect", [
     (2, 8, 4, 16, 256, 1),        # 60 tokens: too short to split (needs 8 tiles/partition)
     (1, 8, 32, 16, 256, 4),       # 512 tokens: capped at 32 / 8 partitions
-    (16, 8, 16, 16, 256, 2),      # 128 units -> 2 partitions of 8 tiles
+    (16, 8, 16, 16, 256, 1),      # 128 units, 16 tiles: two rounds of loads beat a split
+    (16, 8, 17, 16, 256, 2),      # 17 tiles: 2 partitions
     (4, 8, 128, 16, 256, 8),      # 32 units -> 8 partitions of 16 tiles
     (1, 8, 1024, 16, 256, 32),    # 8 units -> 32 partitions of 32 tiles
     (32, 8, 1024, 16, 256, 8),    # units fill the CUs: split long rows, 128 tiles each, <= 8
@@ -70,6 +71,8 @@ def test_choose_partitions_properties():
                         # units cover the device: only long rows split, into
                         # partitions of up to 128 tiles, at most 8
                         assert P == min(8, max(1, math.ceil(mb / 128)))
+                    elif mb <= 16:
+                        assert P == 1   # a row of 16 tiles or fewer does not split
                     elif P > 1:
                         # every partition of a full row gets at least 8 tiles
                         assert mb // P >= 8

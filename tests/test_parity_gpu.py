@@ -395,6 +395,8 @@ WIDE_TABLE_CASES = [
     (8, [16, 16, 16, 16, 16, 16, 16, 16], 512),
     (3, [2047, 2048, 2049], 512),
     (1, [130], 4096),
+    (5, [255, 256, 257, 272, 273], 64),   # 16, 16, 17, 17, 18 tiles: around the
+                                          # heuristic's no-split threshold
 ]
 
 
