@@ -23,9 +23,10 @@
 //   columns the G query heads repeated to 16, and the reduction the head dim,
 //   so no cross-lane reduction is needed; lane (row g = lane/16, column
 //   c = lane%16) ends with the scores of tokens 4g..4g+3 for head c % G.  In
-//   the row layout (16-bit elements, D = 128, G <= 4) each MFMA takes whole
-//   rows of 4 tokens, so K loads cover whole cache lines; two DPP adds sum
-//   the row quarters, and lane (g, c) ends with tokens g, g+4, g+8, g+12.
+//   the row layout (16-bit elements, D = 64 or 128, see k_rows_layout) each
+//   MFMA takes whole rows of a few tokens, so K loads cover whole cache
+//   lines; DPP adds sum the row parts, and for D = 128 lane (g, c) ends with
+//   tokens g, g+4, g+8, g+12.
 // * Online softmax per (row g, head): running max m and normaliser l in log2
 //   units (scale * log2 e is folded into one multiply), so each lane updates
 //   its own statistics from its 4 scores with no cross-lane max per tile.  The
@@ -117,13 +118,25 @@ struct Geometry {
 // the whole rows of T = 16 / Q tokens: A row Q t + a is part a of token
 // T j + t, B column T b + hh is part b of the query of head hh % G.  A K load
 // then covers whole cache lines like a V load, and the parts' partial dot
-// products are summed across lanes afterwards.  The G heads times Q parts
-// must fit the 16 columns, and a lane's useful products must fall in its own
-// row of 16 lanes: 16-bit elements with D = 128 (Q = 4, G <= 4) or D = 64
-// (Q = 2, G <= 8).
-template <int DT, int D, int G>
+// products are summed across lanes afterwards.  A lane's useful products
+// must fall in its own row of 16 lanes: 16-bit elements with D = 128 (Q = 4)
+// or D = 64 (Q = 2).  When G exceeds the T heads one set of columns holds,
+// each step runs G / T MFMAs, one per set of T heads (row_query_sets), and
+// the extra MFMAs and selects cost more than the whole-line loads save except
+// for D = 128, G = 8 in the bandwidth-bound modes (a single pass, or a batch
+// covering the device): measured ~10 % faster there, ~0.5 us slower in a
+// split of one long sequence, and slower for G = 16.
+template <int DT, int D, int G, int MODE>
 constexpr bool k_rows_layout() {
-    return PA_K_ROWS && DT != PA_DTYPE_F32 && ((D == 128 && G <= 4) || (D == 64 && G <= 8));
+    if (!PA_K_ROWS || DT == PA_DTYPE_F32) return false;
+    if (D == 64) return G <= 8;
+    if (D == 128) return G <= 4 || (G == 8 && (MODE == kSingle || MODE == kFusedLate));
+    return false;
+}
+// Query operand sets of the row layout: T = 16 / Q heads per set.
+template <int D, int G>
+constexpr int row_query_sets() {
+    return G * (D / 32) <= 16 ? 1 : G * (D / 32) / 16;
 }
 
 // Token of slot r (0..3) of the lanes in MFMA row group g: the scores and V
@@ -268,22 +281,40 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b) {
 //  * D = 128 (Q = 4, T = 4): register `part` holds token 4j + g.
 //  * D = 64 (Q = 2, T = 8): registers `part` and `part` + 2 hold tokens
 //    8j + 2g and 8j + 2g + 1.
-template <int DT, int D>
-__device__ __forceinline__ f32x4 tile_scores_rows(const u32x4 *kr, u32x4 qr, int part) {
+// With NS query sets (qr[set], heads set * T + c16 % T) every step runs NS
+// MFMAs and the lane keeps the score of set `set` = its head's.
+template <int DT, int D, int NS>
+__device__ __forceinline__ f32x4 tile_scores_rows(const u32x4 *kr, const u32x4 *qr, int part,
+                                                  int set) {
     f32x4 s;
     if constexpr (D == 128) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f32x4 c = mfma_16x16x32<DT>(kr[j], qr);
-            const float x = (part & 2) ? ((part & 1) ? c[3] : c[2]) : ((part & 1) ? c[1] : c[0]);
-            s[j] = add_row_ror<4>(add_row_ror<8>(x));
+            float y = 0.f;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                const f32x4 c = mfma_16x16x32<DT>(kr[j], qr[n]);
+                const float x =
+                    (part & 2) ? ((part & 1) ? c[3] : c[2]) : ((part & 1) ? c[1] : c[0]);
+                const float z = add_row_ror<4>(add_row_ror<8>(x));
+                y = NS == 1 || set == n ? z : y;
+            }
+            s[j] = y;
         }
     } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const f32x4 c = mfma_16x16x32<DT>(kr[j], qr);
-            s[2 * j] = add_row_ror<8>(part ? c[1] : c[0]);
-            s[2 * j + 1] = add_row_ror<8>(part ? c[3] : c[2]);
+            float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                const f32x4 c = mfma_16x16x32<DT>(kr[j], qr[n]);
+                const float z0 = add_row_ror<8>(part ? c[1] : c[0]);
+                const float z1 = add_row_ror<8>(part ? c[3] : c[2]);
+                y0 = NS == 1 || set == n ? z0 : y0;
+                y1 = NS == 1 || set == n ? z1 : y1;
+            }
+            s[2 * j] = y0;
+            s[2 * j + 1] = y1;
         }
     }
     return s;
@@ -543,9 +574,10 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr int KL = Geo::kKLoads, VE = Geo::kVElems, VW = Geo::kVWords;
     constexpr int VLD = Geo::kVLoads, VWIDTH = Geo::kVWidth;
     constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate;
-    constexpr bool kRows = k_rows_layout<DT, D, G>();
-    constexpr int QL = kRows ? 1 : KL;  // query registers (16 bytes each)
+    constexpr bool kRows = k_rows_layout<DT, D, G, MODE>();
     constexpr int kRowsQ = KL, kRowsT = 16 / KL;  // row layout: parts per row, tokens per step
+    constexpr int kSets = row_query_sets<D, G>();   // row layout: query sets of kRowsT heads
+    constexpr int QL = kRows ? kSets : KL;  // query registers (16 bytes each)
 
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
@@ -583,14 +615,17 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // (after the empty partitions have left; loads complete in order, so a
     // query issued behind the first tiles delays their update a little).
     const char *qrow = p.q + ((long long)b * p.H + kvh * G + (c16 % G)) * Geo::kRowBytes;
-    // (row layout: chunk g of part c16 / T of the row, T = 16 / Q tokens per
-    // MFMA step)
+    // (row layout: chunk g of part c16 / T of the row of head
+    // (set * T + c16 % T) % G, T = 16 / Q tokens per MFMA step)
+    const char *qgroup = p.q + ((long long)b * p.H + kvh * G) * Geo::kRowBytes;
     u32x4 qr[QL];
     auto load_query = [&]() {
 #pragma unroll
         for (int m = 0; m < QL; ++m)
             qr[m] = *reinterpret_cast<const u32x4 *>(
-                qrow + (kRows ? 64 * (c16 / kRowsT) : 64 * m) + 16 * g);
+                kRows ? qgroup + ((m * kRowsT + c16 % kRowsT) % G) * Geo::kRowBytes +
+                            64 * (c16 / kRowsT) + 16 * g
+                      : qrow + 64 * m + 16 * g);
     };
     if constexpr (MODE != kFusedLate) load_query();
 
@@ -695,7 +730,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         for (int s = 0; s < DEPTH; ++s) {
             if constexpr (kRows)
                 update_tile<DT, D, G, true>(st,
-                                            tile_scores_rows<DT, D>(kr[s], qr[0], c16 / kRowsT),
+                                            tile_scores_rows<DT, D, kSets>(
+                                                kr[s], qr, c16 / kRowsT, (c16 % G) / kRowsT),
                                             vr[s], p.qk_scale, g, nl[s]);
             else
                 update_tile<DT, D, G, false>(st, tile_scores<DT, D>(kr[s], qr), vr[s],

@@ -569,6 +569,21 @@ def test_many_kv_heads(gpu, dtype):
         assert_close(to_f64(out), oracle.decode_case(case), dtype, f"Hkv=64 P={parts}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_group_of_8_in_covering_batch(gpu, dtype):
+    # 64 query / 8 kv heads (G = 8, d = 128): a single pass and, with 40 x 8
+    # units covering the device, the late-query fused mode whose long rows
+    # split -- the modes that read K in whole rows for G = 8
+    lens = [3000, 17, 0, 2048] + [int(x) for x in np.random.default_rng(15).integers(1, 400, 36)]
+    need = sum(math.ceil(n / 16) for n in lens)
+    case = pi.make_case(40, lens, 64, 8, 128, 16, dtype=dtype, seed=15, pool=need + 3)
+    ref = oracle.decode_case(case)
+    for parts in (0, 1):
+        say(f"G=8 covering batch {dtype} P={parts}")
+        out = run_gpu(case, gpu, num_partitions=parts)
+        assert_close(to_f64(out), ref, dtype, f"G=8 B=40 P={parts}")
+
+
 @pytest.mark.parametrize("parts", [0, 1, 4])
 def test_context_lens_are_clamped(gpu, parts):
     # a length beyond max_blocks * block_size counts as the full row and a
