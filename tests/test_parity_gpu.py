@@ -569,6 +569,18 @@ def test_many_kv_heads(gpu, dtype):
         assert_close(to_f64(out), oracle.decode_case(case), dtype, f"Hkv=64 P={parts}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("parts", [0, 1, 2, 4])
+def test_trailing_minus_one_padding(gpu, dtype, parts):
+    # workload 1's shape with a second, shorter row: a table 4 blocks wide whose
+    # row for 20 tokens ends in -1 entries past its two blocks, on a pool of 6
+    case = pi.make_case(2, [60, 20], 32, 8, 128, 16, dtype=dtype, seed=16, max_blocks=4, pool=6)
+    assert (case.block_tables[1, 2:] == -1).all() and (case.block_tables[0] >= 0).all()
+    say(f"-1 padding {dtype} P={parts}")
+    out = run_gpu(case, gpu, num_partitions=parts)
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"-1 padding P={parts}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_group_of_8_in_covering_batch(gpu, dtype):
     # 64 query / 8 kv heads (G = 8, d = 128): a single pass and, with 40 x 8
