@@ -123,7 +123,9 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
 /*
  * pa_decode with the choices exposed.
  *   num_partitions   0 = heuristic (as pa_decode), 1 = single pass, n > 1 =
- *                    P = min(n, T, 4096) partitions, split as above.
+ *                    P = min(n, W, 4096) partitions, W = max_blocks *
+ *                    block_size / 16 the tiles of a table row, split as
+ *                    above.
  *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
  *                    treated like -1 instead of being read (a guard against
  *                    out-of-range ids).
@@ -173,11 +175,12 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
 /*
  * The launch heuristic (pure; no HIP call).  Work units are the B * Hkv
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
- * they are fewer than num_cus it splits each unit's T tiles into enough
+ * they are fewer than num_cus it splits the W = max_blocks * block_size / 16
+ * tiles of a table row into enough
  * partitions to give about num_cus workgroups, keeping at least 8 tiles (128
  * tokens) per partition of a full row; a row of at most 16 tiles (256
  * tokens) does not split.  When they already cover the device it
- * returns ceil(T / 128), at most 8: room for the long sequences of the batch
+ * returns ceil(W / 128), at most 8: room for the long sequences of the batch
  * to split into partitions of about 2048 tokens (see Partitions).  Returns
  * >= 1 (1 for non-positive inputs or block_size below 16).
  */

@@ -9,8 +9,9 @@
 // * One workgroup per (kvh, b[, partition]) serves all G = H / Hkv query heads
 //   of the group, so each K/V row is read from HBM once per kv head, not once
 //   per query head.
-// * A wave consumes one 16-token tile per step; partition p takes a
-//   sequence's tiles p, p + P, ... and its 4 waves every 4th of those.  Block
+// * A wave consumes 16-token tiles, two in flight at a time (one group); a
+//   sequence's tiles are dealt in runs of 2 to the 4 * busy (partition, wave)
+//   lanes in turn, busy being the partitions its length fills.  Block
 //   ids are read with scalar loads one group of tiles ahead, so they are
 //   wave-uniform and each tile gets a raw buffer descriptor (SGPRs) over
 //   exactly its live rows of head kvh; the per-lane offsets never change.
