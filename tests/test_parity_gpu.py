@@ -418,13 +418,14 @@ def test_short_contexts_in_wide_table(gpu, dtype, shape, parts):
             assert (out[b].float() == 0).all()
 
 
-def expected_partials(case, P, ref_max=None):
+def expected_partials(case, P, ref_max=None, busy_of=None):
     """Per-partition (max, sum, weighted sum) from the header's split rule,
     computed directly in fp64.  Sequence b's n tiles are dealt in runs of 2
-    tiles to 4 * busy lanes in turn (busy = min(n, P)); partition p owns lanes
-    4p .. 4p + 3.  With scores s = scale * q.K * log2(e): m = max s,
-    l = sum 2^(s - r), O = sum 2^(s - r) V where r = ref_max[b, h, p] when
-    given (else m); partitions owning no live token give (-1e30, 0, 0)."""
+    tiles to 4 * busy lanes in turn (busy = busy_of(n), by default min(n, P));
+    partition p owns lanes 4p .. 4p + 3.  With scores s = scale * q.K *
+    log2(e): m = max s, l = sum 2^(s - r), O = sum 2^(s - r) V where
+    r = ref_max[b, h, p] when given (else m); partitions owning no live token
+    give (-1e30, 0, 0)."""
     B, H, d = case.q.shape
     G = H // case.num_kv_heads
     bs = case.block_size
@@ -434,7 +435,7 @@ def expected_partials(case, P, ref_max=None):
     for b in range(B):
         ctx = int(case.context_lens[b])
         n = (ctx + 15) // 16
-        busy = min(n, P)
+        busy = min(n, P) if busy_of is None else busy_of(n)
         owner = [((j // 2) % (4 * busy)) // 4 for j in range(n)]
         for p in range(P):
             toks = [t for j in range(n) if owner[j] == p
@@ -457,25 +458,20 @@ def expected_partials(case, P, ref_max=None):
     return m, l, o
 
 
-def test_partials_follow_documented_split(gpu):
-    case = pi.make_case(4, [83, 16, 0, 700], 8, 2, 128, 16, dtype="f32", seed=77,
-                        max_blocks=50, pool=60)
-    P = 8
-    d = DeviceCase(case, gpu)
-    nbytes = pa.pa_workspace_bytes(case.batch, 8, 128, P)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
-    say("partials layout and split rule")
-    pa.pa_decode_partials(*d.args(), P, 0, ws, nbytes)
-    torch.cuda.synchronize()
-    ml_bytes = case.batch * 8 * P * 8
+def read_partials(ws, B, H, P, d):
+    """(max, sum) pairs and partial sums from a workspace, per the header's layout."""
+    ml_bytes = B * H * P * 8
     acc_off = (ml_bytes + 255) // 256 * 256
     host = ws.cpu()
-    ml = host[:ml_bytes].view(torch.float32).view(case.batch, 8, P, 2).double().numpy()
-    acc = host[acc_off:acc_off + case.batch * 8 * P * 128 * 4].view(torch.float32)
-    acc = acc.view(case.batch, 8, P, 128).double().numpy()
-    # the header's contract: l and O are sums relative to the reported reference
-    # max m, which lies within 8 below the partition's largest score
-    m, l, o = expected_partials(case, P, ref_max=ml[..., 0])
+    ml = host[:ml_bytes].view(torch.float32).view(B, H, P, 2).double().numpy()
+    acc = host[acc_off:acc_off + B * H * P * d * 4].view(torch.float32)
+    return ml, acc.view(B, H, P, d).double().numpy()
+
+
+def check_partials(case, ml, acc, P, busy_of=None):
+    """The header's partials contract against a direct fp64 computation; returns
+    the mask of empty partitions."""
+    m, l, o = expected_partials(case, P, ref_max=ml[..., 0], busy_of=busy_of)
     empty = l == 0
     assert (ml[..., 0][empty] == np.float32(-1e30)).all() and (ml[..., 1][empty] == 0).all()
     assert (acc[empty] == 0).all()
@@ -487,6 +483,52 @@ def test_partials_follow_documented_split(gpu):
     vmax = np.abs(case.v_cache).max()
     err = np.abs(acc - o).max(axis=-1)
     assert (err[live] <= 1e-4 * l[live] * vmax).all()
+    return empty
+
+
+def test_heuristic_split_follows_documented_rule(gpu):
+    # pa_decode_ex with the heuristic count and a caller workspace runs the
+    # split kernel (every partition writes its slot) and the merge kernel; the
+    # partials show the heuristic's per-sequence rule: at most 16 tiles stay
+    # whole, longer rows use min(P, ceil(n / 8)) partitions (units < CUs)
+    lens = [83, 16, 0, 700, 300]
+    case = pi.make_case(5, lens, 8, 2, 128, 16, dtype="f32", seed=78, max_blocks=200,
+                        pool=sum(math.ceil(n / 16) for n in lens) + 2)
+    cus = pa.pa_device_num_cus(0)
+    P = pa.pa_choose_partitions(case.batch, 2, 200, 16, cus)
+    assert case.batch * 2 < cus and P > 1
+    d = DeviceCase(case, gpu)
+    nbytes = pa.pa_workspace_bytes(case.batch, 8, 128, P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    out = torch.empty_like(d.q)
+    say(f"heuristic split rule, P={P}")
+    pa.pa_decode_ex(out, *d.args(), None, 0, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(case), "f32", "heuristic + merge kernel")
+    ml, acc = read_partials(ws, case.batch, 8, P, 128)
+    rule = lambda n: min(n, 1) if n <= 16 else min(P, math.ceil(n / 8))
+    empty = check_partials(case, ml, acc, P, busy_of=rule)
+    # 83 tokens (6 tiles) and 16 tokens stay in partition 0; 700 tokens (44
+    # tiles) use 6 partitions, 300 tokens (19 tiles) 3
+    for b, busy in ((0, 1), (1, 1), (3, 6), (4, 3)):
+        assert (~empty[b, :, :busy]).all() and empty[b, :, busy:].all(), b
+    assert empty[2].all()
+
+
+def test_partials_follow_documented_split(gpu):
+    case = pi.make_case(4, [83, 16, 0, 700], 8, 2, 128, 16, dtype="f32", seed=77,
+                        max_blocks=50, pool=60)
+    P = 8
+    d = DeviceCase(case, gpu)
+    nbytes = pa.pa_workspace_bytes(case.batch, 8, 128, P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    say("partials layout and split rule")
+    pa.pa_decode_partials(*d.args(), P, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    # the header's contract: l and O are sums relative to the reported reference
+    # max m, which lies within 8 below the partition's largest score
+    ml, acc = read_partials(ws, case.batch, 8, P, 128)
+    empty = check_partials(case, ml, acc, P)
     # sequence 2 is empty; sequences 1 (one tile) and 0 (6 tiles: three runs,
     # all in partition 0's lanes) use partition 0 only; sequence 3 (44 tiles:
     # 22 runs over 32 lanes) uses partitions 0-5
