@@ -767,8 +767,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr int N = G * VE, N2 = N / 2, N4 = N / 4;
     // A swap of (x, y) hands the upper 32 lanes' x to the lower lanes' y and
     // the lower lanes' y to the upper lanes' x (likewise odd and even rows for
-    // the 16-lane swap): the lower half keeps the first half of the values,
-    // the upper half the second.
+    // the 16-lane swap).  So after swap(a, z) the lower lanes hold (own a,
+    // upper a) and the upper lanes (lower z, own z): the sum of the pair is
+    // the lower half's total of a and the upper half's of z, with no select.
     float half[N2];
 #pragma unroll
     for (int j = 0; j < N2; ++j) {
@@ -776,15 +777,14 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         const float z = st.acc[(N2 + j) / VE][(N2 + j) % VE] * fh[(N2 + j) / VE];
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(z),
                                                         false, false);
-        half[j] = g >= 2 ? z + __uint_as_float(r[0]) : a + __uint_as_float(r[1]);
+        half[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
     float quarter[N4];
 #pragma unroll
     for (int j = 0; j < N4; ++j) {
         const auto r = __builtin_amdgcn_permlane16_swap(
             __float_as_uint(half[j]), __float_as_uint(half[N4 + j]), false, false);
-        quarter[j] = (g & 1) ? half[N4 + j] + __uint_as_float(r[0])
-                          : half[j] + __uint_as_float(r[1]);
+        quarter[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
 
     // ---- merge the waves through LDS ------------------------------------------
