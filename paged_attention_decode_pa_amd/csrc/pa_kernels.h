@@ -33,7 +33,8 @@
 //   its own statistics from its 4 scores with no cross-lane max per tile.  The
 //   max is a reference that moves only when a score exceeds it by more than 8
 //   (log2 units, a wave-wide vote), so most tiles skip the rescale of the
-//   state.
+//   state; when it moves it takes the head's max over the 4 rows, so it is
+//   the same in every row.
 // * V accumulate on the vector ALUs in fp32: lane (g, c) holds D / 16 elements
 //   of the V rows of its 4 tokens and accumulates them for all G heads; the
 //   weights of the other heads come from neighbouring lanes by DPP broadcast.
@@ -342,7 +343,9 @@ __device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
     // acc / l whatever its m -- and the wave skips the rescale, and its wait
     // for this tile's max, on almost every tile.
     if (__builtin_amdgcn_ballot_w64(bm > st.m + kRescaleSlack) != 0) {
-        const float mn = fmaxf(st.m, bm);
+        // the new reference is the head's max over all 4 rows, so it stays the
+        // same in every row and the epilogue merges the rows without rescaling
+        const float mn = fmaxf(st.m, rows_max(bm));
         const float alpha = fast_exp2(st.m - mn);
         st.l *= alpha;
         st.m = mn;
@@ -747,23 +750,17 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 
     // ---- merge the 4 row groups of the wave -----------------------------------
     // The (m, l) of row g and head h sit in the lanes of row g whose column is
-    // h modulo G.  The maxima and normalisers are combined over the rows in
-    // every lane; the N = G * VE rescaled accumulators of a lane are
-    // reduce-scattered: row g ends with the totals of values [g N/4,
-    // (g + 1) N/4), value i standing for head i / VE, slot i % VE.
-    float mh[G], lh[G], fh[G];
+    // h modulo G.  A head's reference max is the same in the 4 rows
+    // (update_tile), so the normalisers are summed over the rows in every lane
+    // and the N = G * VE accumulators of a lane are reduce-scattered as they
+    // are: row g ends with the totals of values [g N/4, (g + 1) N/4), value i
+    // standing for head i / VE, slot i % VE.
+    float mh[G], lh[G];
     static_for<G>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         mh[h] = group_bcast<G, h>(st.m);
-        lh[h] = group_bcast<G, h>(st.l);
+        lh[h] = rows_sum(group_bcast<G, h>(st.l));
     });
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float M = rows_max(mh[h]);
-        fh[h] = fast_exp2(mh[h] - M);
-        lh[h] = rows_sum(lh[h] * fh[h]);
-        mh[h] = M;
-    }
     constexpr int N = G * VE, N2 = N / 2, N4 = N / 4;
     // A swap of (x, y) hands the upper 32 lanes' x to the lower lanes' y and
     // the lower lanes' y to the upper lanes' x (likewise odd and even rows for
@@ -773,8 +770,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     float half[N2];
 #pragma unroll
     for (int j = 0; j < N2; ++j) {
-        const float a = st.acc[j / VE][j % VE] * fh[j / VE];
-        const float z = st.acc[(N2 + j) / VE][(N2 + j) % VE] * fh[(N2 + j) / VE];
+        const float a = st.acc[j / VE][j % VE];
+        const float z = st.acc[(N2 + j) / VE][(N2 + j) % VE];
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(z),
                                                         false, false);
         half[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
