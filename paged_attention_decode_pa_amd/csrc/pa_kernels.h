@@ -611,6 +611,18 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // Independent loads first: the context length, the first group's table
     // entries and the query all leave before any of them is waited for.
     int ctx = p.lens[b];
+    if constexpr (MODE == kFusedLate) {
+        // With the units covering the device most partitions past the first
+        // are empty: those leave on the length alone, before any table load.
+        if (part > 0) {
+            const int c = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
+            const int nt = (int)(((unsigned)c + kTile - 1) / kTile);
+            const int w = nt > p.solo_tiles
+                              ? (nt + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2
+                              : (nt > 0 ? 1 : 0);
+            if (part >= w) return;
+        }
+    }
     int raw0[DEPTH];
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) raw0[s] = table_at(first + s);
