@@ -94,8 +94,9 @@ enum {
  * length fills, busy_b = min(P, ceil(n_b / T)), T = 8 tiles while the B * Hkv
  * (sequence, kv head) units are fewer than the device's compute units (and
  * busy_b = 1 for n_b <= 16: one workgroup reads 16 tiles in two rounds of
- * loads, faster than a split and its merge) and T = 128 otherwise, so that in
- * a batch that already covers the device only long sequences split.
+ * loads, faster than a split and its merge) and T = 64 otherwise, with
+ * busy_b = 1 for n_b <= 128, so that in a batch that already covers the device
+ * only sequences longer than 2048 tokens split.
  * Partitions p >= busy_b are empty.
  *
  * One decode step (the signature the docs page's kernel launch wraps:
@@ -180,8 +181,9 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
  * partitions to give about num_cus workgroups, keeping at least 8 tiles (128
  * tokens) per partition of a full row; a row of at most 16 tiles (256
  * tokens) does not split.  When they already cover the device it
- * returns ceil(W / 128), at most 8: room for the long sequences of the batch
- * to split into partitions of about 2048 tokens (see Partitions).  Returns
+ * returns 1 for W <= 128, else ceil(W / 64), at most 16: room for the
+ * sequences longer than 2048 tokens to split into partitions of 1024 tokens
+ * (see Partitions).  Returns
  * >= 1 (1 for non-positive inputs or block_size below 16).
  */
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);

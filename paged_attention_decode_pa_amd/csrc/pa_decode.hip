@@ -21,12 +21,14 @@ using namespace pa_detail;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kMinTilesPerPartitionLog2 = 3;  // 8 tiles, 128 tokens
 constexpr int kMinTilesPerPartition = 1 << kMinTilesPerPartitionLog2;
-// When the (sequence, kv head) units alone cover the device, only sequences
-// much longer than a partition of this many tiles (2048 tokens) split, and
-// into at most kMaxLongSplit partitions: a long sequence in a batch of short
+// When the (sequence, kv head) units alone cover the device, a sequence of at
+// most kLongUnsplitTiles tiles (2048 tokens) stays whole -- a uniform batch
+// then needs no merge -- and a longer one splits into partitions of 64 tiles
+// (1024 tokens), at most kMaxLongSplit: a long sequence in a batch of short
 // ones otherwise sets the pace on its own.
-constexpr int kLongPartitionTilesLog2 = 7;  // 128 tiles
-constexpr int kMaxLongSplit = 8;
+constexpr int kLongUnsplitTiles = 128;
+constexpr int kLongPartitionTilesLog2 = 6;  // 64 tiles
+constexpr int kMaxLongSplit = 16;
 // A sequence of at most this many tiles is read by one workgroup in two rounds
 // of loads (4 waves x 2 tiles); splitting it saves at most one round trip,
 // less than the split's store-ticket-reload chain costs, so the heuristic
@@ -273,6 +275,7 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
     const long long tiles = (long long)max_blocks * block_size / kTile;
     if (tiles > 0x7FFFFFFF) return 1;
     if (units >= num_cus) {
+        if (tiles <= kLongUnsplitTiles) return 1;
         const long long P = (tiles + (1LL << kLongPartitionTilesLog2) - 1) >> kLongPartitionTilesLog2;
         return P < kMaxLongSplit ? (int)P : kMaxLongSplit;
     }
@@ -333,11 +336,11 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         if (cus < 0) return cus;
         P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
         // a sequence uses the partitions its length fills: at least 8 tiles
-        // each (none of 16 tiles or fewer splits), 128 when the units alone
-        // cover the device
+        // each (none of 16 tiles or fewer splits), or, when the units alone
+        // cover the device, 64 tiles each (none of 128 tiles or fewer splits)
         const bool covered = (long long)B * Hkv >= cus;
         part_tiles_log2 = covered ? kLongPartitionTilesLog2 : kMinTilesPerPartitionLog2;
-        solo_tiles = covered ? 0 : kUnsplitMaxTiles;
+        solo_tiles = covered ? kLongUnsplitTiles : kUnsplitMaxTiles;
         // with the units covering the device most partitions are empty
         if (covered) fused_mode = kFusedLate;
     } else {

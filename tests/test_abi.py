@@ -43,10 +43,11 @@ def test_strerror_covers_codes():
     (16, 8, 17, 16, 256, 2),      # 17 tiles: 2 partitions
     (4, 8, 128, 16, 256, 8),      # 32 units -> 8 partitions of 16 tiles
     (1, 8, 1024, 16, 256, 32),    # 8 units -> 32 partitions of 32 tiles
-    (32, 8, 1024, 16, 256, 8),    # units fill the CUs: split long rows, 128 tiles each, <= 8
+    (32, 8, 1024, 16, 256, 16),   # units fill the CUs: split long rows, 64 tiles each, <= 16
     (32, 8, 64, 16, 256, 1),      # ... a row of 64 tiles does not split
-    (64, 8, 300, 16, 256, 3),     # ... 300 tiles -> 3
-    (64, 8, 100000, 16, 256, 8),  # ... at most 8
+    (32, 8, 128, 16, 256, 1),     # ... nor one of 128 (2048 tokens)
+    (64, 8, 300, 16, 256, 5),     # ... 300 tiles -> 5
+    (64, 8, 100000, 16, 256, 16),  # ... at most 16
     (1, 1, 100, 16, 256, 12),     # capped at 100 // 8 = 12 (runs of 8 or 9 tiles)
     (1, 8, 7, 16, 256, 1),
     (0, 8, 10, 16, 256, 1),
@@ -68,9 +69,9 @@ def test_choose_partitions_properties():
                     P = pa.pa_choose_partitions(B, Hkv, mb, 16, cus)
                     assert 1 <= P <= max(1, mb)
                     if B * Hkv >= cus:
-                        # units cover the device: only long rows split, into
-                        # partitions of up to 128 tiles, at most 8
-                        assert P == min(8, max(1, math.ceil(mb / 128)))
+                        # units cover the device: only rows over 128 tiles
+                        # split, into partitions of up to 64 tiles, at most 16
+                        assert P == (1 if mb <= 128 else min(16, math.ceil(mb / 64)))
                     elif mb <= 16:
                         assert P == 1   # a row of 16 tiles or fewer does not split
                     elif P > 1:
