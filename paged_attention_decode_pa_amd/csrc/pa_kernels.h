@@ -608,20 +608,24 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         return trow[e < p.max_blocks ? e : p.max_blocks - 1];
     };
 
+    // Tiles of a context length (clamped to the table row), and the
+    // partitions a sequence of nt tiles asks for (capped at P below).
+    auto tiles_of = [&](int len) -> int {
+        const int c = len < 0 ? 0 : (len > p.max_tiles * kTile ? p.max_tiles * kTile : len);
+        return (int)(((unsigned)c + kTile - 1) / kTile);
+    };
+    auto partitions_for = [&](int nt) -> int {
+        return nt > p.solo_tiles ? (nt + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2
+                                 : (nt > 0 ? 1 : 0);
+    };
+
     // Independent loads first: the context length, the first group's table
     // entries and the query all leave before any of them is waited for.
     int ctx = p.lens[b];
     if constexpr (MODE == kFusedLate) {
         // With the units covering the device most partitions past the first
         // are empty: those leave on the length alone, before any table load.
-        if (part > 0) {
-            const int c = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
-            const int nt = (int)(((unsigned)c + kTile - 1) / kTile);
-            const int w = nt > p.solo_tiles
-                              ? (nt + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2
-                              : (nt > 0 ? 1 : 0);
-            if (part >= w) return;
-        }
+        if (part > 0 && part >= partitions_for(tiles_of(ctx))) return;
     }
     int raw0[DEPTH];
 #pragma unroll
@@ -645,13 +649,11 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     };
     if constexpr (MODE != kFusedLate) load_query();
 
+    const int ntiles = tiles_of(ctx);
     ctx = ctx < 0 ? 0 : (ctx > p.max_tiles * kTile ? p.max_tiles * kTile : ctx);
-    const int ntiles = (int)(((unsigned)ctx + kTile - 1) / kTile);
     // Partitions holding tiles (the first `busy`); the fused merge waits for
     // exactly these.
-    const int want = ntiles > p.solo_tiles
-                         ? (ntiles + (1 << p.part_tiles_log2) - 1) >> p.part_tiles_log2
-                         : (ntiles > 0 ? 1 : 0);
+    const int want = partitions_for(ntiles);
     const int busy = want < p.P ? want : p.P;
     const bool idle = part >= busy;             // owns no tile
     const int stride = busy * NW * DEPTH;       // tiles between a lane's runs
