@@ -515,6 +515,34 @@ def test_heuristic_split_follows_documented_rule(gpu):
     assert empty[2].all()
 
 
+def test_heuristic_split_in_covering_batch(gpu):
+    # with the units covering the device the heuristic leaves sequences of at
+    # most 128 tiles whole and splits longer ones into 64-tile partitions
+    lens = [0, 16, 2048, 2049, 5000] + [40] * 35
+    case = pi.make_case(len(lens), lens, 8, 8, 128, 16, dtype="f32", seed=79,
+                        pool=sum(math.ceil(n / 16) for n in lens) + 2)
+    cus = pa.pa_device_num_cus(0)
+    B, W = case.batch, case.max_blocks
+    P = pa.pa_choose_partitions(B, 8, W, 16, cus)
+    assert B * 8 >= cus and P == min(16, math.ceil(W / 64))
+    d = DeviceCase(case, gpu)
+    nbytes = pa.pa_workspace_bytes(B, 8, 128, P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    out = torch.empty_like(d.q)
+    say(f"heuristic split, covering batch, P={P}")
+    pa.pa_decode_ex(out, *d.args(), None, 0, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(case), "f32", "covering + merge kernel")
+    ml, acc = read_partials(ws, B, 8, P, 128)
+    rule = lambda n: min(n, 1) if n <= 128 else min(P, math.ceil(n / 64))
+    empty = check_partials(case, ml, acc, P, busy_of=rule)
+    # 2048 tokens (128 tiles) stay whole; 2049 (129 tiles) use 3 partitions,
+    # 5000 (313 tiles) 5
+    for b, busy in ((1, 1), (2, 1), (3, 3), (4, 5), (5, 1)):
+        assert (~empty[b, :, :busy]).all() and empty[b, :, busy:].all(), b
+    assert empty[0].all()
+
+
 def test_partials_follow_documented_split(gpu):
     case = pi.make_case(4, [83, 16, 0, 700], 8, 2, 128, 16, dtype="f32", seed=77,
                         max_blocks=50, pool=60)
