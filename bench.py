@@ -40,6 +40,7 @@ METRIC = "decode step μs and achieved HBM GB/s (% of MI355X peak) per config"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATION_BYTES = 1 << 30       # distinct bytes the copies must span
 MAX_COPIES = 64
+VARIANT = None                 # ablation library to time instead (--variant)
 
 
 def log(msg):
@@ -56,6 +57,9 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--variant", default=None, choices=["valu_qk"],
+                    help="time an ablation build instead of the library: valu_qk runs the "
+                         "q.K product on the vector ALUs instead of the matrix cores")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (counter scale)")
     ap.add_argument("--sweep", nargs="?", const="design-note", default=None,
@@ -106,7 +110,7 @@ class Workload:
         tiles = c.max_blocks * c.block_size // 16   # partitions split 16-token tiles
         self.P = max(1, min(self.P, tiles, 4096))   # the library's partition limit
         self.num_partitions = num_partitions
-        self.lib = pa.load()
+        self.lib = pa.load_variant(VARIANT) if VARIANT else pa.load()
 
     def step(self, i, stream):
         """One whole decode step on copy i % N (pa_decode / pa_decode_ex)."""
@@ -403,7 +407,9 @@ def sweep(dev, steps, warmup, use_graph):
 
 
 def main():
+    global VARIANT
     args = parse()
+    VARIANT = args.variant
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step has no multi-GPU path in this library)", file=sys.stderr)
@@ -414,6 +420,8 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     pa.load()
+    if VARIANT:
+        pa.load_variant(VARIANT)
     dev = torch.device("cuda:0")
     use_graph = not args.eager
     if args.sweep:
@@ -496,12 +504,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(c.name),
+            "traffic": None if VARIANT else recorded_traffic(c.name),
             "avg_launch_us": round(t_dom * 1e6, 3),
             "launches_per_step": 1,
             "bytes_per_launch": dom_bytes,
         },
         "cpu_baseline": base,
+        "library": (f"ablation build {VARIANT} ({os.path.basename(pa.VARIANT_PATHS[VARIANT])})"
+                    if VARIANT else os.path.basename(pa.LIB_PATH)),
         "max_abs_err": err,
         "per_config": per_config,
     }

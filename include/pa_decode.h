@@ -112,8 +112,14 @@ enum {
  * buffer and the ticket buffer (zeroed when allocated; every call leaves its
  * tickets zero) are allocated on first need per (device, stream) and grown
  * when larger ones are needed (growing synchronises `stream` once).  Calls on
- * one stream are ordered by the stream; do not capture the first call on a
- * stream into a graph (it allocates).  pa_release frees them.
+ * one stream are ordered by the stream.  Graph capture: do not capture the
+ * first call on a stream (it allocates).  A captured call keeps the addresses
+ * of the buffers of the stream it was captured on, so (a) replay such a graph
+ * only where it cannot overlap other work that uses that stream's buffers
+ * (any call on that stream, or another replay), and (b) capture again after
+ * a larger call on that stream or pa_release, both of which may free the
+ * buffers; a caller workspace (pa_decode_ex) avoids both.  pa_release frees
+ * them.
  * max_blocks is the width of block_tables (its row stride).
  * Returns PA_OK or a negative PA_ERR_* code.
  */

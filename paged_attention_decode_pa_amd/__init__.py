@@ -16,6 +16,8 @@ from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa_decode.so")
+# Ablation builds of the same sources (see build.py), loaded only on request.
+VARIANT_PATHS = {"valu_qk": os.path.join(HERE, "libpa_decode_valu_qk.so")}
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
@@ -77,6 +79,13 @@ def load(path: Optional[str] = None):
     if path is None:
         _lib = lib
     return lib
+
+
+def load_variant(name: str):
+    """Load an ablation build by name (raises if it is not built)."""
+    if name not in VARIANT_PATHS:
+        raise ValueError(f"unknown library variant {name!r}; known: {sorted(VARIANT_PATHS)}")
+    return load(VARIANT_PATHS[name])
 
 
 def _ptr(x) -> Optional[int]:

@@ -3,6 +3,12 @@
 The kernels of each element type are a translation unit of their own
 (csrc/pa_kernels_<dtype>.hip) and compile in parallel with the host launcher
 (csrc/pa_decode.hip); the objects are then linked into libpa_decode.so.
+
+An ablation library, libpa_decode_valu_qk.so, is built beside it from the same
+sources with PA_QK_VALU=1: the q.K product of the 16-bit, head-dim-128,
+4-heads-per-kv-head kernels on the vector ALUs instead of the matrix cores,
+all else identical.  It exists only to measure what the matrix cores bring
+(bench.py --variant valu_qk); the package never loads it by itself.
 """
 import os
 import subprocess
@@ -16,6 +22,10 @@ SOURCES = [os.path.join(CSRC, f) for f in
            ("pa_decode.hip", "pa_kernels_f32.hip", "pa_kernels_bf16.hip", "pa_kernels_f16.hip")]
 KERNEL_SOURCES = SOURCES[1:]
 LIB = os.path.join(HERE, "libpa_decode.so")
+# name -> (library file, extra compiler flags)
+VARIANTS = {
+    "valu_qk": (os.path.join(HERE, "libpa_decode_valu_qk.so"), ["-DPA_QK_VALU=1"]),
+}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -31,38 +41,57 @@ def _clean(stderr: str) -> str:
     return "\n".join(l for l in stderr.splitlines() if _NOISE not in l)
 
 
-def compile_objects(sources, outdir, extra=()):
-    """Compile each source to an object in outdir, all at once.  Returns
-    [(source, object, returncode, stderr)]."""
+def compile_objects_async(sources, outdir, extra=()):
+    """Start compiling each source to an object in outdir.  Returns
+    [(source, object, Popen)]."""
     procs = []
     for src in sources:
         obj = os.path.join(outdir, os.path.basename(src) + ".o")
         cmd = [HIPCC, *FLAGS, *INCLUDES, *extra, "-c", src, "-o", obj]
         procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                  stderr=subprocess.PIPE, text=True)))
+    return procs
+
+
+def compile_objects(sources, outdir, extra=()):
+    """Compile each source to an object in outdir, all at once.  Returns
+    [(source, object, returncode, stderr)]."""
     results = []
-    for src, obj, p in procs:
+    for src, obj, p in compile_objects_async(sources, outdir, extra):
         _, err = p.communicate()
         results.append((src, obj, p.returncode, err))
     return results
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, variants=tuple(VARIANTS)) -> str:
+    """Compile and link libpa_decode.so and the named ablation libraries (all
+    objects compile in parallel).  Returns the path of libpa_decode.so."""
+    jobs = [(LIB, [])] + [VARIANTS[v] for v in variants]
     with tempfile.TemporaryDirectory() as tmp:
         if verbose:
-            print(f"{HIPCC} {' '.join(FLAGS)} -c <each of {len(SOURCES)} sources>", flush=True)
-        results = compile_objects(SOURCES, tmp)
-        for src, _, rc, err in results:
-            if rc != 0:
-                raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{_clean(err)}")
-            if verbose and _clean(err).strip():
-                print(_clean(err), file=sys.stderr)
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
-               *[obj for _, obj, _, _ in results], "-o", LIB + ".tmp"]
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"link failed ({res.returncode}):\n{_clean(res.stderr)}")
-    os.replace(LIB + ".tmp", LIB)
+            print(f"{HIPCC} {' '.join(FLAGS)} -c <each of {len(SOURCES)} sources>"
+                  + "".join(f", again with {' '.join(f)} for {os.path.basename(l)}"
+                            for l, f in jobs[1:]), flush=True)
+        procs = []
+        for n, (lib, extra) in enumerate(jobs):
+            outdir = os.path.join(tmp, str(n))
+            os.mkdir(outdir)
+            procs.append((lib, compile_objects_async(SOURCES, outdir, extra)))
+        for lib, pending in procs:
+            objs = []
+            for src, obj, p in pending:
+                _, err = p.communicate()
+                if p.returncode != 0:
+                    raise RuntimeError(f"hipcc failed on {src} for {os.path.basename(lib)} "
+                                       f"({p.returncode}):\n{_clean(err)}")
+                if verbose and _clean(err).strip():
+                    print(_clean(err), file=sys.stderr)
+                objs.append(obj)
+            cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"link failed ({res.returncode}):\n{_clean(res.stderr)}")
+            os.replace(lib + ".tmp", lib)
     return LIB
 
 

@@ -322,6 +322,73 @@ __device__ __forceinline__ f32x4 tile_scores_rows(const u32x4 *kr, const u32x4 *
     return s;
 }
 
+#ifndef PA_QK_VALU
+#define PA_QK_VALU 0
+#endif
+// Build option for measuring the matrix cores' worth (0 in the library):
+// with PA_QK_VALU=1 the row layout's q.K for 16-bit elements, D = 128 and
+// G = 4 runs on the vector ALUs instead (tile_scores_rows_valu), everything
+// else unchanged.
+template <int DT, int D, int G, bool ROWS>
+constexpr bool valu_scores() {
+    return PA_QK_VALU && ROWS && DT != PA_DTYPE_F32 && D == 128 && G == 4;
+}
+
+// acc + the dot product of 8 16-bit elements (4 packed words) of k and q.
+// (Each word is copied to a scalar before the bit cast: this compiler casts a
+// vector element operand as if it were element 0.)
+template <int DT>
+__device__ __forceinline__ float dot8(u32x4 k, u32x4 q, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned kw = k[i], qw = q[i];
+        if constexpr (DT == PA_DTYPE_BF16)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw),
+                                                  __builtin_bit_cast(bf16x2, qw), acc, false);
+        else
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, kw),
+                                         __builtin_bit_cast(f16x2, qw), acc, false);
+    }
+    return acc;
+}
+
+// Row-layout scores (D = 128, G = 4) on the vector ALUs, in the layout
+// tile_scores_rows returns: slot j of lane (g, c16) is the score of token
+// 4j + g for head c16 % 4.  Load j gives lane (g, c16) elements
+// [32 a + 8 g, + 8) of token 4j + t, a = c16 % 4, t = c16 / 4, and qh[h]
+// holds the same elements of head h's query.  Each lane forms its 4 partial
+// dot products (one per head); two rounds of half swaps (as in the epilogue)
+// reduce-scatter them over the 4 row groups so that row g keeps head g, two
+// DPP adds sum the 4 parts of the quad, and the lane fetches the score of
+// token 4j + g for its head from row c16 % 4, quad g.
+template <int DT>
+__device__ __forceinline__ f32x4 tile_scores_rows_valu(const u32x4 *kr, const u32x4 *qh, int g,
+                                                       int c16) {
+    const int src = 4 * (16 * (c16 & 3) + 4 * g);  // byte address of the source lane
+    f32x4 s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float P[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) P[h] = dot8<DT>(kr[j], qh[h], 0.f);
+        const auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(P[0]),
+                                                         __float_as_uint(P[2]), false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(P[1]),
+                                                         __float_as_uint(P[3]), false, false);
+        const float a0 = __uint_as_float(r0[0]) + __uint_as_float(r0[1]);
+        const float a1 = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+        const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1),
+                                                         false, false);
+        float x = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF,
+                                                        false));  // quad_perm [1,0,3,2]
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF,
+                                                        false));  // quad_perm [2,3,0,1]
+        s[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
+    }
+    return s;
+}
+
 // The softmax update and V accumulation of one tile given its raw scores c
 // (tile_scores or tile_scores_rows): slot r holds token slot_token<D, ROWS>(g,
 // r), whose V row vw[r] is.
@@ -581,7 +648,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr bool kRows = k_rows_layout<DT, D, G, MODE>();
     constexpr int kRowsQ = KL, kRowsT = 16 / KL;  // row layout: parts per row, tokens per step
     constexpr int kSets = row_query_sets<D, G>();   // row layout: query sets of kRowsT heads
-    constexpr int QL = kRows ? kSets : KL;  // query registers (16 bytes each)
+    constexpr bool kValu = valu_scores<DT, D, G, kRows>();
+    constexpr int QL = kValu ? G : (kRows ? kSets : KL);  // query registers (16 bytes each)
 
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
@@ -643,9 +711,10 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int m = 0; m < QL; ++m)
             qr[m] = *reinterpret_cast<const u32x4 *>(
-                kRows ? qgroup + ((m * kRowsT + c16 % kRowsT) % G) * Geo::kRowBytes +
-                            64 * (c16 / kRowsT) + 16 * g
-                      : qrow + 64 * m + 16 * g);
+                kValu   ? qgroup + m * Geo::kRowBytes + 64 * (c16 % kRowsQ) + 16 * g
+                : kRows ? qgroup + ((m * kRowsT + c16 % kRowsT) % G) * Geo::kRowBytes +
+                              64 * (c16 / kRowsT) + 16 * g
+                        : qrow + 64 * m + 16 * g);
     };
     if constexpr (MODE != kFusedLate) load_query();
 
@@ -746,7 +815,10 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         // rows as well, since loads complete in order, and measures slower)
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-            if constexpr (kRows)
+            if constexpr (kValu)
+                update_tile<DT, D, G, true>(st, tile_scores_rows_valu<DT>(kr[s], qr, g, c16),
+                                            vr[s], p.qk_scale, g, nl[s]);
+            else if constexpr (kRows)
                 update_tile<DT, D, G, true>(st,
                                             tile_scores_rows<DT, D, kSets>(
                                                 kr[s], qr, c16 / kRowsT, (c16 % G) / kRowsT),

@@ -29,6 +29,12 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pa.EXPORTS)
 
 
+def test_ablation_library_exports_the_same_functions():
+    lib = pa.load_variant("valu_qk")
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
 def test_strerror_covers_codes():
     for code in range(0, -11, -1):
         s = pa.strerror(code)

@@ -1,0 +1,72 @@
+"""Parity of the ablation build libpa_decode_valu_qk.so (q.K on the vector ALUs
+for 16-bit elements, head dim 128, 4 query heads per kv head) with the fp64
+oracle, through its C ABI, in every kernel mode that build changes: single
+pass, fused split, fused split with the late query (a batch covering the
+device), and the split kernel with the separate merge kernel.  Its timings
+only mean something if it computes the same decode step."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pa_inputs as pi
+import paged_attention_decode_pa_amd as pa
+
+from gpu_util import DeviceCase, assert_close, check_host_preconditions, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_variant(case, dev, parts, workspace=False):
+    check_host_preconditions(case)
+    lib = pa.load_variant("valu_qk")
+    d = DeviceCase(case, dev)
+    out = torch.empty_like(d.q)
+    c = case
+    ws, ws_bytes = None, 0
+    if workspace:
+        P = max(1, min(parts, c.max_blocks * c.block_size // 16, 4096))
+        ws_bytes = pa.pa_workspace_bytes(c.batch, c.num_heads, c.head_dim, P)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    rc = lib.pa_decode_ex(out.data_ptr(), d.q.data_ptr(), d.k.data_ptr(), d.v.data_ptr(),
+                          d.table.data_ptr(), d.lens.data_ptr(), c.batch, c.num_heads,
+                          c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks, float(c.scale),
+                          d.dtype, torch.cuda.current_stream().cuda_stream, parts,
+                          c.num_pool_blocks, None if ws is None else ws.data_ptr(), ws_bytes)
+    assert rc == 0, pa.strerror(rc)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+@pytest.mark.parametrize("parts", [0, 1])
+def test_valu_qk_workloads(gpu, cid, parts):
+    case = pi.make_config_case(cid)
+    say(f"valu_qk workload {cid} P={parts}")
+    out = run_variant(case, gpu, parts)
+    assert_close(to_f64(out), oracle.decode_case(case), case.dtype, f"valu_qk w{cid} P={parts}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("parts,workspace", [(0, False), (1, False), (3, False), (5, True)])
+def test_valu_qk_ragged_with_holes(gpu, dtype, parts, workspace):
+    case = pi.make_case(5, [0, 1, 17, 300, 1000], 32, 8, 128, 16, dtype=dtype, seed=21,
+                        holes=[(3, 4), (4, 0), (4, 30)])
+    say(f"valu_qk ragged {dtype} P={parts} workspace={workspace}")
+    out = run_variant(case, gpu, parts, workspace)
+    assert_close(to_f64(out), oracle.decode_case(case), dtype,
+                 f"valu_qk ragged {dtype} P={parts}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_valu_qk_covering_batch(gpu, dtype):
+    # 40 x 8 units cover the device: the fused mode with the late query load
+    lens = [3000, 17, 0, 2048] + [int(x) for x in np.random.default_rng(22).integers(1, 400, 36)]
+    need = sum(math.ceil(n / 16) for n in lens)
+    case = pi.make_case(40, lens, 32, 8, 128, 16, dtype=dtype, seed=22, pool=need + 3)
+    say(f"valu_qk covering batch {dtype}")
+    out = run_variant(case, gpu, 0)
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"valu_qk covering {dtype}")

@@ -26,3 +26,19 @@ def test_no_kernel_uses_scratch():
     assert sum("pa_merge_kernel" in n for n in names) == 3
     bad = [n for n, s in zip(names, scratch) if s != 0]
     assert not bad, f"kernels using scratch: {bad}"
+
+
+def test_valu_qk_ablation_uses_no_scratch():
+    """The ablation build's changed kernels (16-bit) also keep to registers."""
+    _, flags = hip_build.VARIANTS["valu_qk"]
+    srcs = [s for s in hip_build.KERNEL_SOURCES if "f32" not in s]
+    with tempfile.TemporaryDirectory() as tmp:
+        results = hip_build.compile_objects(
+            srcs, tmp, extra=[*flags, "-Rpass-analysis=kernel-resource-usage"])
+    for src, _, rc, err in results:
+        assert rc == 0, err[-2000:]
+        n = re.findall(r"Function Name: (\S+)", err)
+        s = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", err)]
+        assert len(n) == len(s) and n, src
+        bad = [a for a, b in zip(n, s) if b != 0]
+        assert not bad, f"kernels using scratch: {bad}"
