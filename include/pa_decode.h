@@ -74,7 +74,8 @@ enum {
     PA_ERR_UNSUPPORTED = -3, /* valid but not built: d, block_size or H/Hkv       */
     PA_ERR_DTYPE = -4,       /* dtype is not a pa_dtype_t value                   */
     PA_ERR_ALIGN = -5,       /* a pointer breaks the alignment rule               */
-    PA_ERR_WORKSPACE = -6,   /* caller workspace missing or too small             */
+    PA_ERR_WORKSPACE = -6,   /* workspace missing or too small, or the library   */
+                             /* would have to allocate one during graph capture */
     PA_ERR_HIP = -7,         /* a HIP runtime call or a launch failed             */
     PA_ERR_DEVICE = -8,      /* no current HIP device                             */
     PA_ERR_ALIAS = -9,       /* out overlaps an input                             */
@@ -108,18 +109,25 @@ enum {
  * a library-owned workspace and takes an atomic ticket; the last workgroup of
  * each (sequence, kv head) merges those partials and writes out.  A sequence
  * with at most one non-empty partition is written directly by partition 0
- * (zeros for an empty sequence); empty partitions do nothing.  The partials
- * buffer and the ticket buffer (zeroed when allocated; every call leaves its
- * tickets zero) are allocated on first need per (device, stream) and grown
- * when larger ones are needed (growing synchronises `stream` once).  Calls on
- * one stream are ordered by the stream.  Graph capture: do not capture the
- * first call on a stream (it allocates).  A captured call keeps the addresses
- * of the buffers of the stream it was captured on, so (a) replay such a graph
- * only where it cannot overlap other work that uses that stream's buffers
- * (any call on that stream, or another replay), and (b) capture again after
- * a larger call on that stream or pa_release, both of which may free the
- * buffers; a caller workspace (pa_decode_ex) avoids both.  pa_release frees
- * them.
+ * (zeros for an empty sequence); empty partitions do nothing.
+ *
+ * Library-owned buffers.  The partials buffer and the ticket buffer are
+ * allocated on first need per (device, stream) and grown when larger ones are
+ * needed; growing synchronises `stream` once.  Tickets are zeroed on `stream`
+ * when allocated, and every call leaves them zero.  Calls on one stream are
+ * ordered by the stream.  Calls from several host threads are safe: the
+ * lookup, any growth and the launch happen under one lock.  pa_release frees
+ * the buffers.
+ *
+ * Graph capture.  A call that would allocate or grow the buffers while
+ * `stream` is being captured returns PA_ERR_WORKSPACE, so make one call of
+ * the same or a larger shape on that stream first.  A captured call keeps the
+ * addresses of its stream's buffers.  So (a) replay such a graph only where
+ * it cannot overlap other work that uses them (any call on that stream, or
+ * another replay), and (b) capture again after a larger call on that stream
+ * or pa_release, either of which may free them.  A caller workspace
+ * (pa_decode_ex) avoids both.
+ *
  * max_blocks is the width of block_tables (its row stride).
  * Returns PA_OK or a negative PA_ERR_* code.
  */

@@ -138,11 +138,17 @@ int device_cus(int dev) {
     return cus;
 }
 
+// The caller holds g_mutex, and keeps holding it until the work using the
+// buffers is enqueued: a concurrent call on the same stream that grows them
+// then frees them only after that work (it synchronises the stream first).
 int library_buffers(int dev, hipStream_t stream, size_t partial_bytes, size_t num_tickets,
                     void **partials, int **tickets) {
-    std::lock_guard<std::mutex> lock(g_mutex);
     LibBuffers &lb = g_buffers[{dev, stream}];
     if (lb.partial_bytes < partial_bytes || lb.num_tickets < num_tickets) {
+        // no allocation, synchronisation or memset may land in a graph capture
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return PA_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return PA_ERR_WORKSPACE;
         // the previous buffers may still be in use by work on this stream
         if ((lb.partials || lb.tickets) && hipStreamSynchronize(stream) != hipSuccess)
             return PA_ERR_HIP;
@@ -159,7 +165,10 @@ int library_buffers(int dev, hipStream_t stream, size_t partial_bytes, size_t nu
         lb.tickets = nullptr;
         lb.num_tickets = 0;
         if (hipMalloc(&lb.tickets, num_tickets * sizeof(int)) != hipSuccess) return PA_ERR_HIP;
-        if (hipMemset(lb.tickets, 0, num_tickets * sizeof(int)) != hipSuccess) return PA_ERR_HIP;
+        // zeroed on the stream the kernels run on, so it is ordered before them
+        // even when that stream does not synchronise with the null stream
+        if (hipMemsetAsync(lb.tickets, 0, num_tickets * sizeof(int), stream) != hipSuccess)
+            return PA_ERR_HIP;
         lb.num_tickets = num_tickets;
     }
     *partials = lb.partials;
@@ -304,7 +313,9 @@ const char *pa_strerror(int code) {
                    "16..256, H/Hkv in {1,2,4,8,16})";
         case PA_ERR_DTYPE: return "unknown dtype";
         case PA_ERR_ALIGN: return "pointer alignment (16 bytes for tensors, 4 for int32 arrays)";
-        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_WORKSPACE:
+            return "workspace missing or too small, or the library would allocate one while the "
+                   "stream is being captured";
         case PA_ERR_HIP: return "HIP runtime call or kernel launch failed";
         case PA_ERR_DEVICE: return "no usable HIP device";
         case PA_ERR_ALIAS: return "out overlaps an input";
@@ -363,6 +374,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     }
     void *ws = nullptr;
     int *tickets = nullptr;
+    std::lock_guard<std::mutex> lock(g_mutex);
     if ((rc = library_buffers(dev, s, need, (size_t)B * Hkv, &ws, &tickets)) != PA_OK) return rc;
     attach_workspace(p, ws, d);
     p.counters = tickets;

@@ -268,6 +268,91 @@ def test_graph_replay_matches_eager(gpu):
         assert torch.equal(other, eager)
 
 
+def test_first_fused_call_on_a_fresh_stream(gpu):
+    # the first call on a new (non-blocking) stream allocates and zeroes the
+    # tickets; the zeroing is ordered before the fused kernel on that stream
+    case = pi.make_config_case(5)
+    d = DeviceCase(case, gpu)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    out = torch.empty_like(d.q)
+    say("first fused call on a fresh stream")
+    pa.pa_decode(out, *d.args(), s)
+    s.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", "fresh stream")
+
+
+def test_allocation_during_capture_is_refused(gpu):
+    # a call that would allocate the library buffers while its stream is
+    # being captured returns PA_ERR_WORKSPACE and enqueues nothing
+    case = pi.make_config_case(5)
+    d = DeviceCase(case, gpu)
+    out = torch.zeros_like(d.q)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    lib = pa.load()
+    say("pa_decode during capture of a fresh stream")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        out.fill_(1.0)
+        rc = lib.pa_decode(out.data_ptr(), d.q.data_ptr(), d.k.data_ptr(), d.v.data_ptr(),
+                           d.table.data_ptr(), d.lens.data_ptr(), *d.args()[5:], s.cuda_stream)
+        g.capture_end()
+    torch.cuda.synchronize()
+    assert rc == pa.PA_ERR_WORKSPACE, pa.strerror(rc)
+    g.replay()
+    torch.cuda.synchronize()
+    assert (out.float() == 1.0).all()
+    pa.pa_decode(out, *d.args(), s)  # outside the capture the same call works
+    s.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", "after refused capture")
+
+
+def test_concurrent_callers_on_one_stream(gpu):
+    # host threads share one stream while its library buffers grow (more
+    # heads, then more units); the lock keeps each launch's buffers alive, and
+    # every output equals the single-threaded one bitwise
+    import threading
+    specs = [(1, 4096, 32, 8), (1, 4096, 64, 8), (3, 3000, 32, 16), (2, 6000, 16, 8)]
+    cases = [pi.make_case(B, ctx, H, Hkv, 128, 16, dtype="bf16", seed=60 + i)
+             for i, (B, ctx, H, Hkv) in enumerate(specs)]
+    dcs = [DeviceCase(c, gpu) for c in cases]
+    refs = []
+    for d in dcs:
+        o = torch.empty_like(d.q)
+        pa.pa_decode(o, *d.args(), None)
+        refs.append(o)
+    torch.cuda.synchronize()
+    for c, r in zip(cases, refs):
+        assert_close(to_f64(r), oracle.decode_case(c), "bf16", "single-threaded reference")
+    s = torch.cuda.Stream()
+    reps = 25
+    outs = [[torch.empty_like(d.q) for _ in range(reps)] for d in dcs]
+    errors = []
+
+    def worker(t):
+        try:
+            for r in range(reps):
+                i = (t + r) % len(dcs)
+                pa.pa_decode(outs[i][r], *dcs[i].args(), s)
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    say("4 threads x 25 calls on one stream")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    s.synchronize()
+    assert not errors, errors
+    for t in range(4):
+        for r in range(reps):
+            i = (t + r) % len(dcs)
+            assert torch.equal(outs[i][r], refs[i]), (t, r, i)
+
+
 def test_library_workspace_reused_across_shapes(gpu):
     # one stream's library buffers serve calls of different B, Hkv and P in
     # turn (growing and shrinking); every call must match the oracle
