@@ -35,8 +35,8 @@
  *   - Supported shapes: d in {64, 128, 256} (the benchmark script's head_dim
  *     argument; 128 in every configuration of the docs page); block_size a
  *     power of two from 16 to 256;
- *     H % Hkv == 0 with H / Hkv in {1, 2, 4, 8, 16}.  Others return
- *     PA_ERR_UNSUPPORTED.  Sequences are processed in tiles of 16 tokens; a
+ *     H % Hkv == 0 with H / Hkv in {1, 2, 4, 8, 16}; B * H < 2^31;
+ *     max_blocks * block_size <= 2^30.  Others return PA_ERR_UNSUPPORTED.  Sequences are processed in tiles of 16 tokens; a
  *     row of the table covers T = max_blocks * block_size / 16 tiles.
  *   - All calls only enqueue work on `stream` (a hipStream_t, NULL = the null
  *     stream); nothing synchronises with the host.  The return code reports

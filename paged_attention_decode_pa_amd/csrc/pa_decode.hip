@@ -85,6 +85,8 @@ int validate(void *out, const void *q, const void *k_cache, const void *v_cache,
     const int G = H / Hkv;
     if (!shape_built(dtype, d, G)) return PA_ERR_UNSUPPORTED;
     if ((long long)max_blocks * block_size > (1LL << 30)) return PA_ERR_UNSUPPORTED;
+    // (sequence, head) pairs are counted in 32 bits (tickets, merge groups)
+    if ((long long)B * H > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     v->G = G;
     v->esize = elem_bytes(dtype);
     // a tile's rows of one kv head are addressed with 32-bit buffer offsets

@@ -113,6 +113,7 @@ def call(**kw):
     (dict(d=256, H=128, Hkv=8), pa.PA_ERR_UNSUPPORTED),          # G = 16 at d = 256
     (dict(d=256, H=32, Hkv=8, dtype=0), pa.PA_ERR_UNSUPPORTED),  # fp32, G = 4 at d = 256
     (dict(Hkv=1 << 20, H=1 << 20), pa.PA_ERR_UNSUPPORTED),      # tile offsets past 2^31
+    (dict(B=1 << 26, H=64, Hkv=8), pa.PA_ERR_UNSUPPORTED),      # 2^32 (sequence, head) pairs
     (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=48), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=512), pa.PA_ERR_UNSUPPORTED),
