@@ -46,6 +46,14 @@
 //   the workspace; then either a separate merge kernel combines them, or (fused
 //   mode) the last workgroup of each (b, kvh) to finish -- found with an atomic
 //   ticket -- combines them with the same rule and writes out.
+//
+// Build-time settings (macros).  libpa_decode.so is built with the defaults;
+// the other values exist only to measure the alternatives the defaults were
+// chosen over: PA_WAVES_PER_GROUP (4), PA_PIPELINE_DEPTH (2 tiles in flight
+// per wave), PA_K_ROWS (1 = the row K layout where k_rows_layout picks it,
+// 0 = the column layout everywhere), PA_KV_CACHE_POLICY (2 = non-temporal
+// K/V loads) and PA_QK_VALU (0; 1 = the vector-ALU q.K of the ablation
+// library libpa_decode_valu_qk.so, which is built and tested).
 #ifndef PA_KERNELS_H
 #define PA_KERNELS_H
 
