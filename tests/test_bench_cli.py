@@ -1,0 +1,29 @@
+"""bench.py's host-side contract on the CPU: it refuses more than one GPU
+before touching one, and its oracle baseline leg reports what it measured."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
+
+
+def test_cpu_baseline_fields():
+    base = bench.cpu_baseline(1, 0.2)
+    assert base["kind"] == "oracle" and base["unit"] == "GB/s"
+    assert base["value"] > 0 and base["cores"] >= 1 and base["ms_per_step"] > 0
+    assert "workload-1" in base["sample"]
+
+
+def test_recorded_traffic_needs_matching_workload():
+    assert bench.recorded_traffic("no such workload") is None
