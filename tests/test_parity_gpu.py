@@ -653,8 +653,13 @@ def test_partials_follow_documented_split(gpu):
 def random_case(seed):
     """A seeded random draw over the built shape space: dtype, head dim, group
     size, block size, batch, ragged lengths (zeros included), holes, partitions
-    (0 = heuristic) and which split path runs."""
+    (0 = heuristic) and which split path runs.  One draw in five (from a
+    generator of its own, so the other draws are unchanged) is a batch of
+    33-80 sequences over 8 kv heads, whose units cover the device: the
+    heuristic then takes the late-query fused mode."""
     rng = np.random.default_rng(seed)
+    wide = np.random.default_rng(seed + 1_000_000)
+    covering = bool(wide.random() < 0.2)
     dtype = ["f32", "bf16", "f16"][rng.integers(3)]
     d = [64, 128, 256][rng.integers(3)]
     G = [1, 2, 4, 8, 16][rng.integers(5)]
@@ -665,6 +670,10 @@ def random_case(seed):
     B = int(rng.integers(1, 7))
     max_len = int(rng.choice([40, 300, 3000]))
     lens = [int(x) for x in rng.integers(0, max_len + 1, size=B)]
+    if covering:
+        Hkv, B = 8, int(wide.integers(33, 81))
+        lens = [int(x) for x in wide.integers(0, 301, size=B)]
+        lens[int(wide.integers(B))] = int(wide.integers(2049, 4001))  # one that splits
     max_blocks = max(1, max(math.ceil(n / bs) for n in lens)) + int(rng.integers(0, 3))
     holes = []
     for b, n in enumerate(lens):
