@@ -104,7 +104,10 @@ enum {
  * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
  * shape parameters).  Picks the number of context partitions P with
  * pa_choose_partitions for the current device.  P == 1 runs one kernel that
- * writes out directly.  P > 1 runs the split kernel in its fused form: every
+ * writes out directly; when the B * Hkv (sequence, kv head) units fill at most
+ * half of the device's compute units (and d >= 128), it runs two workgroups
+ * per unit, each reading all of K and one half of every V row and writing
+ * that half of the output.  P > 1 runs the split kernel in its fused form: every
  * workgroup of a non-empty partition writes its (max, sum, weighted values) to
  * a library-owned workspace and takes an atomic ticket; the last workgroup of
  * each (sequence, kv head) merges those partials and writes out.  A sequence

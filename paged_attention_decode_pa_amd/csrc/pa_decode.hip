@@ -365,7 +365,14 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     p.part_tiles_log2 = part_tiles_log2;
     p.solo_tiles = solo_tiles;
     p.out = out;
-    if (P == 1) return run_main(p, dtype, d, v.G, kSingle, s);
+    if (P == 1) {
+        // A single pass whose units fill at most half of the compute units
+        // runs as two workgroups per unit, each with half of V's head dim.
+        const int cus = device_cus(dev);
+        if (cus < 0) return cus;
+        const bool split_v = split_v_built(d) && 2LL * B * Hkv <= cus;
+        return run_main(p, dtype, d, v.G, split_v ? kSingleSplitV : kSingle, s);
+    }
     const size_t need = workspace_layout(B, H, P, d).total;
     if (workspace) {
         // caller workspace: split kernel, then the merge kernel (no tickets)

@@ -29,7 +29,17 @@ constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;  // waves per workgroup
 // with the query loaded only once a partition knows it has tiles: used when
 // most partitions of a launch are empty (units covering the device, long
 // sequences only splitting), so that those leave without loading it.
-enum Mode { kSingle = 0, kPartials = 1, kFused = 2, kFusedLate = 3 };
+// kSingleSplitV is the single pass with the head dim of V cut in two: two
+// workgroups per (kv head, sequence) (grid z = 2), each reading all of K for
+// the scores and one half of every V row, and writing that half of the
+// output.  It spreads a single pass that would leave at least half of the
+// compute units idle over twice as many; the second K read of a pair mostly
+// hits the XCD's L2, since both workgroups run on one XCD at the same time.
+enum Mode { kSingle = 0, kPartials = 1, kFused = 2, kFusedLate = 3, kSingleSplitV = 4 };
+
+// kSingleSplitV is built for head dims of at least 128 (a half row then still
+// gives each lane whole 8- or 16-byte V loads).
+constexpr bool split_v_built(int d) { return d >= 128; }
 
 struct Params {
     const char *q;

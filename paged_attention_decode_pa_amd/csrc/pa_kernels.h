@@ -42,7 +42,8 @@
 //   accumulators reduce-scattered, a quarter to each row), the waves through
 //   LDS, always with the rescale-and-sum rule
 //   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)).  A single
-//   pass writes O / L.  With partitions, each workgroup writes (M, L, O) to
+//   pass writes O / L (in kSingleSplitV two workgroups per unit each do so for
+//   one half of the head dim of V).  With partitions, each workgroup writes (M, L, O) to
 //   the workspace; then either a separate merge kernel combines them, or (fused
 //   mode) the last workgroup of each (b, kvh) to finish -- found with an atomic
 //   ticket -- combines them with the same rule and writes out.
@@ -140,7 +141,9 @@ template <int DT, int D, int G, int MODE>
 constexpr bool k_rows_layout() {
     if (!PA_K_ROWS || DT == PA_DTYPE_F32) return false;
     if (D == 64) return G <= 8;
-    if (D == 128) return G <= 4 || (G == 8 && (MODE == kSingle || MODE == kFusedLate));
+    if (D == 128)
+        return G <= 4 ||
+               (G == 8 && (MODE == kSingle || MODE == kSingleSplitV || MODE == kFusedLate));
     return false;
 }
 // Query operand sets of the row layout: T = 16 / Q heads per set.
@@ -399,12 +402,13 @@ __device__ __forceinline__ f32x4 tile_scores_rows_valu(const u32x4 *kr, const u3
 
 // The softmax update and V accumulation of one tile given its raw scores c
 // (tile_scores or tile_scores_rows): slot r holds token slot_token<D, ROWS>(g,
-// r), whose V row vw[r] is.
-template <int DT, int D, int G, bool ROWS>
-__device__ __forceinline__ void update_tile(WaveState<G, D / 16> &st, f32x4 c,
-                                            const unsigned (*vw)[Geometry<DT, D>::kVWords],
+// r), whose V row (or the DV-element slice of it this workgroup serves) vw[r]
+// is.
+template <int DT, int D, int G, bool ROWS, int DV = D>
+__device__ __forceinline__ void update_tile(WaveState<G, DV / 16> &st, f32x4 c,
+                                            const unsigned (*vw)[Geometry<DT, DV>::kVWords],
                                             float qk_scale, int g, int nlive) {
-    using Geo = Geometry<DT, D>;
+    using Geo = Geometry<DT, DV>;  // of the V slice (DV = D, or D / 2 when V is split)
     constexpr int VE = Geo::kVElems;
     float s[4];
 #pragma unroll
@@ -650,8 +654,15 @@ __device__ __forceinline__ void merge_group(const Params &p, int b, int kvh, int
 template <int DT, int D, int G, int NW, int DEPTH, int MODE>
 __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     using Geo = Geometry<DT, D>;
-    constexpr int KL = Geo::kKLoads, VE = Geo::kVElems, VW = Geo::kVWords;
-    constexpr int VLD = Geo::kVLoads, VWIDTH = Geo::kVWidth;
+    // V slices per row (kSingleSplitV: this workgroup serves elements
+    // [vslice * DV, (vslice + 1) * DV) of V and of the output)
+    constexpr int VS = MODE == kSingleSplitV ? 2 : 1;
+    constexpr int DV = D / VS;
+    static_assert(VS == 1 || split_v_built(D), "V split needs a head dim of 128 or more");
+    using GeoV = Geometry<DT, DV>;
+    constexpr int KL = Geo::kKLoads, VE = GeoV::kVElems, VW = GeoV::kVWords;
+    constexpr int VLD = GeoV::kVLoads, VWIDTH = GeoV::kVWidth;
+    constexpr bool kSinglePass = MODE == kSingle || MODE == kSingleSplitV;
     constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate;
     constexpr bool kRows = k_rows_layout<DT, D, G, MODE>();
     constexpr int kRowsQ = KL, kRowsT = 16 / KL;  // row layout: parts per row, tokens per step
@@ -662,7 +673,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
     const int b = p.b0 + blockIdx.y;
-    const int part = blockIdx.z;
+    const int part = VS > 1 ? 0 : blockIdx.z;
+    const int vslice = VS > 1 ? blockIdx.z : 0;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
     const int lane = threadIdx.x % kWave;
     const int c16 = lane & 15;  // MFMA column / token of the tile for K
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // One busy partition (or none) writes the output itself, as a single pass;
     // in the fused mode a partition without tiles adds nothing to the merge
     // and writes nothing (partition 0 of an empty sequence writes zeros).
-    const bool direct = MODE == kSingle || (kFusedMerge && busy <= 1);
+    const bool direct = kSinglePass || (kFusedMerge && busy <= 1);
     const bool silent = kFusedMerge && part >= max(busy, 1);
 
     // Per-lane byte offsets inside one tile's rows of head kvh; never change.
@@ -760,7 +772,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             voff[r][s] = slot_token<D, kRows>(g, r) * p.tok_bytes + VWIDTH * c16 +
                          16 * VWIDTH * s;
     const char *kbase = p.k + kvh * Geo::kRowBytes;
-    const char *vbase = p.v + kvh * Geo::kRowBytes;
+    const char *vbase = p.v + kvh * Geo::kRowBytes + vslice * GeoV::kRowBytes;
 
     WaveState<G, VE> st;
     st.m = kMaxInit;
@@ -824,15 +836,15 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
             if constexpr (kValu)
-                update_tile<DT, D, G, true>(st, tile_scores_rows_valu<DT>(kr[s], qr, g, c16),
+                update_tile<DT, D, G, true, DV>(st, tile_scores_rows_valu<DT>(kr[s], qr, g, c16),
                                             vr[s], p.qk_scale, g, nl[s]);
             else if constexpr (kRows)
-                update_tile<DT, D, G, true>(st,
+                update_tile<DT, D, G, true, DV>(st,
                                             tile_scores_rows<DT, D, kSets>(
                                                 kr[s], qr, c16 / kRowsT, (c16 % G) / kRowsT),
                                             vr[s], p.qk_scale, g, nl[s]);
             else
-                update_tile<DT, D, G, false>(st, tile_scores<DT, D>(kr[s], qr), vr[s],
+                update_tile<DT, D, G, false, DV>(st, tile_scores<DT, D>(kr[s], qr), vr[s],
                                              p.qk_scale, g, nl[s]);
             nl[s] = live_tokens(nbase + s, nid[s]);
             // (tiles past the context are issued too, with empty ranges: a
@@ -880,11 +892,11 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 
     // ---- merge the waves through LDS ------------------------------------------
     __shared__ float2 sm_ml[NW][G];
-    __shared__ float sm_acc[NW][G][D];
+    __shared__ float sm_acc[NW][G][DV];
 #pragma unroll
     for (int j = 0; j < N4; ++j) {
         const int i = g * N4 + j;
-        sm_acc[wave][i / VE][acc_elem<DT, D>(c16, i % VE)] = quarter[j];
+        sm_acc[wave][i / VE][acc_elem<DT, DV>(c16, i % VE)] = quarter[j];
     }
     if (lane == 0) {
 #pragma unroll
@@ -892,9 +904,10 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     }
     __syncthreads();
 
-    // Thread t handles head h = idx / (D / 2) and elements 2 (idx % (D / 2)) + {0, 1}.
-    for (int idx = threadIdx.x; idx < G * (D / 2); idx += NW * kWave) {
-        const int h = idx / (D / 2), e = 2 * (idx % (D / 2));
+    // Thread t handles head h = idx / (DV / 2) and elements 2 (idx % (DV / 2)) + {0, 1}
+    // of this workgroup's slice.
+    for (int idx = threadIdx.x; idx < G * (DV / 2); idx += NW * kWave) {
+        const int h = idx / (DV / 2), e = 2 * (idx % (DV / 2));
         float M = kMaxInit;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][h].x);
@@ -911,7 +924,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             // nothing to write
         } else if (direct) {
             const float inv = L > 0.f ? 1.f / L : 0.f;
-            store_pair<DT>(p.out, bh * D + e, o0 * inv, o1 * inv);
+            store_pair<DT>(p.out, bh * D + vslice * DV + e, o0 * inv, o1 * inv);
         } else if constexpr (MODE == kPartials) {
             *reinterpret_cast<float2 *>(p.part_acc + (bh * p.P + part) * D + e) =
                 make_float2(o0, o1);
@@ -963,7 +976,8 @@ template <int DT, int D, int G, int MODE>
 hipError_t launch_instance(const Params &p, int nseq, hipStream_t stream) {
     if constexpr (shape_built(DT, D, G)) {
         hipLaunchKernelGGL((pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
-                           dim3(p.Hkv, nseq, p.P), dim3(kWavesPerGroup * kWave), 0, stream, p);
+                           dim3(p.Hkv, nseq, MODE == kSingleSplitV ? 2 : p.P),
+                           dim3(kWavesPerGroup * kWave), 0, stream, p);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;
@@ -986,6 +1000,9 @@ template <int DT, int D>
 hipError_t dispatch_mode(const Params &p, int G, int mode, int nseq, hipStream_t stream) {
     switch (mode) {
         case kSingle: return dispatch_g<DT, D, kSingle>(p, G, nseq, stream);
+        case kSingleSplitV:
+            if constexpr (split_v_built(D)) return dispatch_g<DT, D, kSingleSplitV>(p, G, nseq, stream);
+            else return hipErrorInvalidValue;
         case kPartials: return dispatch_g<DT, D, kPartials>(p, G, nseq, stream);
         case kFused: return dispatch_g<DT, D, kFused>(p, G, nseq, stream);
         default: return dispatch_g<DT, D, kFusedLate>(p, G, nseq, stream);

@@ -353,6 +353,25 @@ def test_concurrent_callers_on_one_stream(gpu):
             assert torch.equal(outs[i][r], refs[i]), (t, r, i)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_single_pass_around_split_v_threshold(gpu, dtype, d):
+    # a single pass whose units fill at most half of the compute units splits
+    # V's head dim over two workgroups (d >= 128); one unit more than that
+    # does not.  Both sides of the threshold, ragged, with a hole.
+    cus = pa.pa_device_num_cus(0)
+    units_split = cus // 2
+    G = 2
+    for Hkv, B in ((8, units_split // 8), (8, units_split // 8 + 1)):
+        lens = [int(x) for x in np.random.default_rng(B + d).integers(0, 250, size=B)]
+        lens[0] = 256
+        case = pi.make_case(B, lens, G * Hkv, Hkv, d, 16, dtype=dtype, seed=B + d,
+                            max_blocks=16, holes=[(0, 3)])
+        say(f"single pass {dtype} d={d} B={B} Hkv={Hkv} (units {B * Hkv}, CUs {cus})")
+        out = run_gpu(case, gpu, num_partitions=1)
+        assert_close(to_f64(out), oracle.decode_case(case), dtype, f"B={B} d={d}")
+
+
 def test_library_workspace_reused_across_shapes(gpu):
     # one stream's library buffers serve calls of different B, Hkv and P in
     # turn (growing and shrinking); every call must match the oracle
