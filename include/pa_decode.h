@@ -110,7 +110,10 @@ enum {
  * that half of the output.  P > 1 runs the split kernel in its fused form: every
  * workgroup of a non-empty partition writes its (max, sum, weighted values) to
  * a library-owned workspace and takes an atomic ticket; the last workgroup of
- * each (sequence, kv head) merges those partials and writes out.  A sequence
+ * each (sequence, kv head) merges those partials and writes out.  When the
+ * B * Hkv * P workgroups fill at most half of the compute units (and
+ * d >= 128), each partition is again served by two workgroups, one per half
+ * of V's head dim, and the ticket counts both.  A sequence
  * with at most one non-empty partition is written directly by partition 0
  * (zeros for an empty sequence); empty partitions do nothing.
  *

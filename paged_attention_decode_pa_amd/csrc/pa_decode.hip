@@ -381,6 +381,13 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         if ((rc = run_main(p, dtype, d, v.G, kPartials, s)) != PA_OK) return rc;
         return run_merge(out, workspace, B, H, P, d, dtype, s);
     }
+    if (fused_mode == kFused && split_v_built(d)) {
+        // a split whose workgroups fill at most half of the compute units
+        // also splits V's head dim over two workgroups per partition
+        const int cus = device_cus(dev);
+        if (cus < 0) return cus;
+        if (2LL * B * Hkv * P <= cus) fused_mode = kFusedSplitV;
+    }
     void *ws = nullptr;
     int *tickets = nullptr;
     std::lock_guard<std::mutex> lock(g_mutex);

@@ -35,9 +35,21 @@ constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;  // waves per workgroup
 // output.  It spreads a single pass that would leave at least half of the
 // compute units idle over twice as many; the second K read of a pair mostly
 // hits the XCD's L2, since both workgroups run on one XCD at the same time.
-enum Mode { kSingle = 0, kPartials = 1, kFused = 2, kFusedLate = 3, kSingleSplitV = 4 };
+// kFusedSplitV does the same for the fused split (grid z = 2 P, z = 2 part +
+// slice): each slice stores its half of a partition's sums (slice 0 also the
+// (max, sum) pair), a unit's ticket counts the arrivals of both slices, and
+// the last of them merges the whole head dim.
+enum Mode {
+    kSingle = 0,
+    kPartials = 1,
+    kFused = 2,
+    kFusedLate = 3,
+    kSingleSplitV = 4,
+    kFusedSplitV = 5
+};
+constexpr int v_slices(int mode) { return mode == kSingleSplitV || mode == kFusedSplitV ? 2 : 1; }
 
-// kSingleSplitV is built for head dims of at least 128 (a half row then still
+// The V-split modes are built for head dims of at least 128 (a half row then still
 // gives each lane whole 8- or 16-byte V loads).
 constexpr bool split_v_built(int d) { return d >= 128; }
 

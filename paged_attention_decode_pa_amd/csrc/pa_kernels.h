@@ -43,7 +43,8 @@
 //   LDS, always with the rescale-and-sum rule
 //   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)).  A single
 //   pass writes O / L (in kSingleSplitV two workgroups per unit each do so for
-//   one half of the head dim of V).  With partitions, each workgroup writes (M, L, O) to
+//   one half of the head dim of V; kFusedSplitV splits V the same way in the
+//   fused split).  With partitions, each workgroup writes (M, L, O) to
 //   the workspace; then either a separate merge kernel combines them, or (fused
 //   mode) the last workgroup of each (b, kvh) to finish -- found with an atomic
 //   ticket -- combines them with the same rule and writes out.
@@ -656,14 +657,14 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     using Geo = Geometry<DT, D>;
     // V slices per row (kSingleSplitV: this workgroup serves elements
     // [vslice * DV, (vslice + 1) * DV) of V and of the output)
-    constexpr int VS = MODE == kSingleSplitV ? 2 : 1;
+    constexpr int VS = v_slices(MODE);
     constexpr int DV = D / VS;
     static_assert(VS == 1 || split_v_built(D), "V split needs a head dim of 128 or more");
     using GeoV = Geometry<DT, DV>;
     constexpr int KL = Geo::kKLoads, VE = GeoV::kVElems, VW = GeoV::kVWords;
     constexpr int VLD = GeoV::kVLoads, VWIDTH = GeoV::kVWidth;
     constexpr bool kSinglePass = MODE == kSingle || MODE == kSingleSplitV;
-    constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate;
+    constexpr bool kFusedMerge = MODE == kFused || MODE == kFusedLate || MODE == kFusedSplitV;
     constexpr bool kRows = k_rows_layout<DT, D, G, MODE>();
     constexpr int kRowsQ = KL, kRowsT = 16 / KL;  // row layout: parts per row, tokens per step
     constexpr int kSets = row_query_sets<D, G>();   // row layout: query sets of kRowsT heads
@@ -673,8 +674,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
     const int b = p.b0 + blockIdx.y;
-    const int part = VS > 1 ? 0 : blockIdx.z;
-    const int vslice = VS > 1 ? blockIdx.z : 0;
+    const int part = VS > 1 ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
+    const int vslice = VS > 1 ? (int)(blockIdx.z & 1) : 0;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
     const int lane = threadIdx.x % kWave;
     const int c16 = lane & 15;  // MFMA column / token of the tile for K
@@ -930,8 +931,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
                 make_float2(o0, o1);
             if (e == 0) p.part_ml[bh * p.P + part] = make_float2(M, L);
         } else {
-            store_pair_coherent(p.part_acc + (bh * p.P + part) * D + e, o0, o1);
-            if (e == 0)
+            // (with V split, each slice stores its half; slice 0 the (max, sum))
+            store_pair_coherent(p.part_acc + (bh * p.P + part) * D + vslice * DV + e, o0, o1);
+            if (e == 0 && vslice == 0)
                 store_pair_coherent(reinterpret_cast<float *>(p.part_ml + bh * p.P + part), M, L);
         }
     }
@@ -939,7 +941,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
         // Publish this partition (its coherent stores complete before the
-        // barrier), take a ticket; the last of the `busy` workgroups of
+        // barrier), take a ticket; the last of the VS * `busy` workgroups of
         // (b, kvh) merges their partitions and resets the ticket for the next
         // call.
         __shared__ int sm_last;
@@ -948,7 +950,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         if (threadIdx.x == 0) {
             const int prev = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1,
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sm_last = prev == busy - 1;
+            sm_last = prev == VS * busy - 1;
         }
         __syncthreads();
         if (sm_last) {
@@ -976,7 +978,7 @@ template <int DT, int D, int G, int MODE>
 hipError_t launch_instance(const Params &p, int nseq, hipStream_t stream) {
     if constexpr (shape_built(DT, D, G)) {
         hipLaunchKernelGGL((pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
-                           dim3(p.Hkv, nseq, MODE == kSingleSplitV ? 2 : p.P),
+                           dim3(p.Hkv, nseq, v_slices(MODE) * p.P),
                            dim3(kWavesPerGroup * kWave), 0, stream, p);
         return hipGetLastError();
     } else {
@@ -1002,6 +1004,9 @@ hipError_t dispatch_mode(const Params &p, int G, int mode, int nseq, hipStream_t
         case kSingle: return dispatch_g<DT, D, kSingle>(p, G, nseq, stream);
         case kSingleSplitV:
             if constexpr (split_v_built(D)) return dispatch_g<DT, D, kSingleSplitV>(p, G, nseq, stream);
+            else return hipErrorInvalidValue;
+        case kFusedSplitV:
+            if constexpr (split_v_built(D)) return dispatch_g<DT, D, kFusedSplitV>(p, G, nseq, stream);
             else return hipErrorInvalidValue;
         case kPartials: return dispatch_g<DT, D, kPartials>(p, G, nseq, stream);
         case kFused: return dispatch_g<DT, D, kFused>(p, G, nseq, stream);

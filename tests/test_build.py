@@ -21,9 +21,9 @@ def test_no_kernel_uses_scratch():
         names += n
         scratch += s
     # built (d, G) pairs: fp32 5 + 5 + 2, bf16 and fp16 5 + 5 + 4; 4 modes each, and
-    # the single pass with V split for d >= 128 (fp32 5 + 2, bf16 and fp16 5 + 4)
+    # the two V-split modes for d >= 128 (fp32 5 + 2, bf16 and fp16 5 + 4)
     decode = [n for n in names if "pa_decode_kernel" in n]
-    assert len(decode) == (12 + 14 + 14) * 4 + (7 + 9 + 9)
+    assert len(decode) == (12 + 14 + 14) * 4 + (7 + 9 + 9) * 2
     assert sum("pa_merge_kernel" in n for n in names) == 3
     bad = [n for n, s in zip(names, scratch) if s != 0]
     assert not bad, f"kernels using scratch: {bad}"

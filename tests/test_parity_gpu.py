@@ -372,6 +372,25 @@ def test_single_pass_around_split_v_threshold(gpu, dtype, d):
         assert_close(to_f64(out), oracle.decode_case(case), dtype, f"B={B} d={d}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_fused_split_around_split_v_threshold(gpu, dtype, d):
+    # a fused split whose B * Hkv * P workgroups fill at most half of the
+    # compute units serves each partition with two workgroups (one per half of
+    # V's head dim); one partition more than that does not.  Ragged lengths,
+    # an empty sequence and a hole; forced counts around the threshold.
+    cus = pa.pa_device_num_cus(0)
+    B, Hkv = 2, 4
+    p_split = cus // (2 * B * Hkv)
+    case = pi.make_case(B, [3000, 0], 2 * Hkv, Hkv, d, 16, dtype=dtype, seed=d + 5,
+                        holes=[(0, 40)])
+    ref = oracle.decode_case(case)
+    for parts in (p_split - 1, p_split, p_split + 1):
+        say(f"fused split {dtype} d={d} P={parts} (workgroups {B * Hkv * parts}, CUs {cus})")
+        out = run_gpu(case, gpu, num_partitions=parts)
+        assert_close(to_f64(out), ref, dtype, f"P={parts} d={d}")
+
+
 def test_library_workspace_reused_across_shapes(gpu):
     # one stream's library buffers serve calls of different B, Hkv and P in
     # turn (growing and shrinking); every call must match the oracle
