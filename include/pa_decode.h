@@ -111,7 +111,7 @@ enum {
  * workgroup of a non-empty partition writes its (max, sum, weighted values) to
  * a library-owned workspace and takes an atomic ticket; the last workgroup of
  * each (sequence, kv head) merges those partials and writes out.  When the
- * B * Hkv * P workgroups fill at most half of the compute units (and
+ * B * Hkv * P workgroups fill at most a quarter of the compute units (and
  * d >= 128), each partition is again served by two workgroups, one per half
  * of V's head dim, and the ticket counts both.  A sequence
  * with at most one non-empty partition is written directly by partition 0

@@ -382,11 +382,13 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         return run_merge(out, workspace, B, H, P, d, dtype, s);
     }
     if (fused_mode == kFused && split_v_built(d)) {
-        // a split whose workgroups fill at most half of the compute units
-        // also splits V's head dim over two workgroups per partition
+        // a split whose workgroups fill at most a quarter of the compute
+        // units also splits V's head dim over two workgroups per partition
+        // (measured: 32 -> 64 workgroups gains ~5 %; 128 -> 256 loses 10-18 %,
+        // the doubled K reads then costing more than the halved V saves)
         const int cus = device_cus(dev);
         if (cus < 0) return cus;
-        if (2LL * B * Hkv * P <= cus) fused_mode = kFusedSplitV;
+        if (4LL * B * Hkv * P <= cus) fused_mode = kFusedSplitV;
     }
     void *ws = nullptr;
     int *tickets = nullptr;

@@ -375,13 +375,13 @@ def test_single_pass_around_split_v_threshold(gpu, dtype, d):
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [128, 256])
 def test_fused_split_around_split_v_threshold(gpu, dtype, d):
-    # a fused split whose B * Hkv * P workgroups fill at most half of the
+    # a fused split whose B * Hkv * P workgroups fill at most a quarter of the
     # compute units serves each partition with two workgroups (one per half of
     # V's head dim); one partition more than that does not.  Ragged lengths,
     # an empty sequence and a hole; forced counts around the threshold.
     cus = pa.pa_device_num_cus(0)
     B, Hkv = 2, 4
-    p_split = cus // (2 * B * Hkv)
+    p_split = cus // (4 * B * Hkv)
     case = pi.make_case(B, [3000, 0], 2 * Hkv, Hkv, d, 16, dtype=dtype, seed=d + 5,
                         holes=[(0, 40)])
     ref = oracle.decode_case(case)
