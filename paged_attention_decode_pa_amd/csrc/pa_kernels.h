@@ -655,8 +655,8 @@ __device__ __forceinline__ void merge_group(const Params &p, int b, int kvh, int
 template <int DT, int D, int G, int NW, int DEPTH, int MODE>
 __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     using Geo = Geometry<DT, D>;
-    // V slices per row (kSingleSplitV: this workgroup serves elements
-    // [vslice * DV, (vslice + 1) * DV) of V and of the output)
+    // V slices per row (the V-split modes: this workgroup serves elements
+    // [vslice * DV, (vslice + 1) * DV) of V, of the output and of the partials)
     constexpr int VS = v_slices(MODE);
     constexpr int DV = D / VS;
     static_assert(VS == 1 || split_v_built(D), "V split needs a head dim of 128 or more");
@@ -671,7 +671,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     constexpr bool kValu = valu_scores<DT, D, G, kRows>();
     constexpr int QL = kValu ? G : (kRows ? kSets : KL);  // query registers (16 bytes each)
 
-    // Grid (Hkv, sequences of this launch, P): kv head fastest in dispatch order.
+    // Grid (Hkv, sequences of this launch, P), or z = 2 part + vslice in the
+    // V-split modes: kv head fastest in dispatch order.
     const int kvh = blockIdx.x;
     const int b = p.b0 + blockIdx.y;
     const int part = VS > 1 ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
