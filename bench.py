@@ -211,9 +211,35 @@ def measure(case, dev, steps, warmup, use_graph, num_partitions=0):
     return w, t_step, max_err
 
 
+def strip_c_comments(text):
+    """C/C++ source without its comments and with each run of whitespace made
+    one space (string and character literals are kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha256():
-    """One digest over the library's sources: every file under csrc/ (sorted by
-    name, each name followed by its bytes) and the C header."""
+    """One digest over the library's code: every file under csrc/ (sorted by
+    name, each name followed by its text) and the C header, with comments and
+    whitespace runs removed, so that edits to comments alone keep it."""
     import hashlib
     csrc = os.path.join(ROOT, "paged_attention_decode_pa_amd", "csrc")
     files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
@@ -221,7 +247,7 @@ def kernel_source_sha256():
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode() + b"\0")
-        h.update(open(f, "rb").read())
+        h.update(strip_c_comments(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

@@ -27,3 +27,14 @@ def test_cpu_baseline_fields():
 
 def test_recorded_traffic_needs_matching_workload():
     assert bench.recorded_traffic("no such workload") is None
+
+
+def test_source_digest_ignores_comments_only():
+    code = 'int a = 1; // one\n/* two */ const char *s = "// kept"; int b = 2;'
+    same = 'int a = 1;   /* other words */\nconst char *s = "// kept";\n// more\nint b = 2;'
+    changed = 'int a = 1; const char *s = "// kept"; int b = 3;'
+    literal = 'int a = 1; const char *s = "/ / kept"; int b = 2;'
+    strip = bench.strip_c_comments
+    assert strip(code) == strip(same)
+    assert strip(code) != strip(changed)
+    assert strip(code) != strip(literal)
