@@ -104,11 +104,9 @@ class Workload:
             self.copies.append(dict(q=q, k=k, v=v, t=t, n=n, out=torch.empty_like(q0)))
         self.dtype = pa.dtype_code(q0.dtype)
         self.cus = pa.pa_device_num_cus(dev.index or 0)
-        self.P = (pa.pa_choose_partitions(c.batch, c.num_kv_heads, c.max_blocks, c.block_size,
-                                          self.cus) if num_partitions == 0
-                  else num_partitions)
-        tiles = c.max_blocks * c.block_size // 16   # partitions split 16-token tiles
-        self.P = max(1, min(self.P, tiles, 4096))   # the library's partition limit
+        # the launch the library makes: partitions, and V slices per partition
+        self.P, self.v_slices = pa.pa_plan(c.batch, c.num_kv_heads, c.head_dim, c.max_blocks,
+                                           c.block_size, self.cus, num_partitions)
         self.num_partitions = num_partitions
         self.lib = pa.load_variant(VARIANT) if VARIANT else pa.load()
 
@@ -132,15 +130,14 @@ class Workload:
 
     def single_launch(self):
         """True when one step is one kernel launch: the single pass, or the
-        fused split (heuristic partitions, library-owned workspace)."""
-        return self.P == 1 or self.num_partitions == 0
+        fused split (every step here uses the library-owned workspace)."""
+        return True
 
     def kernel_name(self):
+        v = ", V split in two" if self.v_slices > 1 else ""
         if self.P == 1:
-            return "pa_decode_kernel (single pass)"
-        if self.num_partitions == 0:
-            return "pa_decode_kernel (split, fused merge)"
-        return "pa_decode_kernel (split) + pa_merge_kernel"
+            return f"pa_decode_kernel (single pass{v})"
+        return f"pa_decode_kernel (split, fused merge{v})"
 
 
 def time_region(fn, steps, warmup, use_graph):
@@ -301,7 +298,8 @@ def point(case, dev, steps, warmup, use_graph, parts):
     """One measured configuration: partition count, µs per step, live GB/s."""
     import torch
     w, ts, err = measure(case, dev, steps, warmup, use_graph, parts)
-    row = dict(partitions=w.P, us=round(ts * 1e6, 3), GBps=round(w.bytes / ts / 1e9, 1),
+    row = dict(partitions=w.P, v_slices=w.v_slices, us=round(ts * 1e6, 3),
+               GBps=round(w.bytes / ts / 1e9, 1),
                max_abs_err=err, algorithmic_bytes=w.bytes)
     del w
     torch.cuda.empty_cache()
@@ -407,6 +405,7 @@ def sweep(dev, steps, warmup, use_graph):
             for label, parts in (("single", 1), ("split", 0)):
                 w, ts, err = measure(case, dev, steps, warmup, use_graph, parts)
                 row[f"{label}_partitions"] = w.P
+                row[f"{label}_v_slices"] = w.v_slices
                 row[f"{label}_us"] = round(ts * 1e6, 3)
                 row[f"{label}_GBps"] = round(w.bytes / ts / 1e9, 1)
                 row[f"{label}_max_abs_err"] = err
@@ -463,8 +462,9 @@ def main():
             w, ts, err = measure(pi.make_config_case(cid), dev, min(args.steps, 1000),
                                  args.warmup, use_graph, parts)
             per_config.append(dict(
-                workload=cid, name=w.case.name, partitions=w.P,
-                path="single-pass" if w.P == 1 else "split-KV + merge",
+                workload=cid, name=w.case.name, partitions=w.P, v_slices=w.v_slices,
+                path=("single-pass" if w.P == 1 else "split-KV + fused merge")
+                     + (", V split in two" if w.v_slices > 1 else ""),
                 us_per_step=round(ts * 1e6, 3), GBps=round(w.bytes / ts / 1e9, 1),
                 pct_of_peak=round(100 * w.bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
                 launches_per_step=1 if w.single_launch() else 2, max_abs_err=err,
@@ -519,6 +519,7 @@ def main():
             "num_heads": c.num_heads, "num_kv_heads": c.num_kv_heads,
             "head_dim": c.head_dim, "block_size": c.block_size,
             "pool_blocks": c.num_pool_blocks, "num_partitions": w.P,
+            "v_slices": w.v_slices,
             "algorithmic_bytes_per_step": w.bytes, "rotation_copies": w.ncopies,
             "timing": "HIP graph replay of K steps" if use_graph else "eager launches",
             "parallelism": "single GPU",

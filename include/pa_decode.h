@@ -103,7 +103,9 @@ enum {
  * One decode step (the signature the docs page's kernel launch wraps:
  * output, query, k_cache, v_cache, block_tables, context_lens plus the scalar
  * shape parameters).  Picks the number of context partitions P with
- * pa_choose_partitions for the current device.  P == 1 runs one kernel that
+ * pa_choose_partitions for the current device, except that P = 2 on a table
+ * of at most 32 tiles becomes P = 1 when the single pass then splits V (see
+ * below): the same two workgroups per unit, without a merge.  P == 1 runs one kernel that
  * writes out directly; when the B * Hkv (sequence, kv head) units fill at most
  * half of the device's compute units (and d >= 128), it runs two workgroups
  * per unit, each reading all of K and one half of every V row and writing
@@ -197,9 +199,9 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
  * The launch heuristic (pure; no HIP call).  Work units are the B * Hkv
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
  * they are fewer than num_cus it splits the W = max_blocks * block_size / 16
- * tiles of a table row into enough
- * partitions to give about num_cus workgroups, keeping at least 8 tiles (128
- * tokens) per partition of a full row; a row of at most 16 tiles (256
+ * tiles of a table row into floor(num_cus / units) partitions, so that the
+ * workgroups never outnumber the compute units, keeping at least 8 tiles
+ * (128 tokens) per partition of a full row; a row of at most 16 tiles (256
  * tokens) does not split.  When they already cover the device it
  * returns 1 for W <= 128, else ceil(W / 64), at most 16: room for the
  * sequences longer than 2048 tokens to split into partitions of 1024 tokens
@@ -207,6 +209,19 @@ size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
  * >= 1 (1 for non-positive inputs or block_size below 16).
  */
 int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
+
+/*
+ * The launch pa_decode_ex makes for these sizes on a device of num_cus compute
+ * units when no caller workspace is given (pure; no HIP call): *partitions =
+ * the context partition count P it uses (num_partitions as in pa_decode_ex:
+ * 0 = heuristic, n > 0 = forced), *v_slices = 2 when each unit (P == 1) or
+ * each partition (P > 1) is served by two workgroups, one per half of V's
+ * head dim, else 1.  Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (B < 0, Hkv,
+ * max_blocks or num_cus <= 0), PA_ERR_VALUE (num_partitions < 0) or
+ * PA_ERR_UNSUPPORTED (d or block_size not supported).
+ */
+int pa_plan(int B, int Hkv, int d, int max_blocks, int block_size, int num_cus,
+            int num_partitions, int *partitions, int *v_slices);
 
 /* Compute units of HIP device `device` (cached), or a negative PA_ERR_*. */
 int pa_device_num_cus(int device);

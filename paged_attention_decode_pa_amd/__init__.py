@@ -36,8 +36,8 @@ PA_ERR_ALIAS = -9
 PA_ERR_VALUE = -10
 
 EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_partials", "pa_merge_partials",
-           "pa_workspace_bytes", "pa_choose_partitions", "pa_device_num_cus", "pa_strerror",
-           "pa_release")
+           "pa_workspace_bytes", "pa_choose_partitions", "pa_plan", "pa_device_num_cus",
+           "pa_strerror", "pa_release")
 
 
 class PaError(RuntimeError):
@@ -68,13 +68,15 @@ def load(path: Optional[str] = None):
     lib.pa_workspace_bytes.argtypes = [I, I, I, I]
     lib.pa_workspace_bytes.restype = SZ
     lib.pa_choose_partitions.argtypes = [I, I, I, I, I]
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.pa_plan.argtypes = [I, I, I, I, I, I, I, IP, IP]
     lib.pa_device_num_cus.argtypes = [I]
     lib.pa_strerror.argtypes = [I]
     lib.pa_strerror.restype = ctypes.c_char_p
     lib.pa_release.argtypes = []
     lib.pa_release.restype = None
     for name in ("pa_decode", "pa_decode_ex", "pa_decode_partials", "pa_merge_partials",
-                 "pa_choose_partitions", "pa_device_num_cus"):
+                 "pa_choose_partitions", "pa_plan", "pa_device_num_cus"):
         getattr(lib, name).restype = I
     if path is None:
         _lib = lib
@@ -166,6 +168,15 @@ def pa_workspace_bytes(B, H, d, num_partitions) -> int:
 
 def pa_choose_partitions(B, Hkv, max_blocks, block_size, num_cus) -> int:
     return int(load().pa_choose_partitions(B, Hkv, max_blocks, block_size, num_cus))
+
+
+def pa_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions=0):
+    """(partitions, v_slices) of the launch pa_decode_ex makes without a caller
+    workspace."""
+    P, vs = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().pa_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions,
+                          ctypes.byref(P), ctypes.byref(vs)), "pa_plan")
+    return P.value, vs.value
 
 
 def pa_device_num_cus(device: int = 0) -> int:

@@ -35,6 +35,9 @@ constexpr int kMaxLongSplit = 16;
 // leaves it whole.
 constexpr int kUnsplitMaxTiles = 16;
 constexpr int kMaxPartitions = 4096;
+// A table of at most this many tiles (512 tokens) that the heuristic would
+// split in two runs as a single pass with V split instead (when allowed).
+constexpr int kShortTableTiles = 32;
 
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 
@@ -276,11 +279,62 @@ int clamp_partitions(int tiles, int P) {
     return P < 1 ? 1 : P;
 }
 
-}  // namespace
+// What pa_decode_ex launches: the partition count, the kernel mode and the
+// per-sequence split rule.
+struct Plan {
+    int P;
+    int mode;
+    int part_tiles_log2;  // (see Params)
+    int solo_tiles;
+};
 
-extern "C" {
+int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
 
-int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {
+Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
+               int num_partitions, bool caller_workspace) {
+    Plan plan{1, kSingle, 0, 0};  // forced counts: every partition up to min(n, P) busy
+    const long long units = (long long)B * Hkv;
+    const bool covered = units >= cus;
+    if (num_partitions == 0) {
+        plan.P = choose_partitions(B, Hkv, max_blocks, block_size, cus);
+        // Two partitions of a short table lose to the single pass with V's
+        // head dim split over the same two workgroups per unit, which needs
+        // no merge (measured at 96-128 units: at 512 tokens the single pass is
+        // 7-8 % faster, at 1024 tokens 4-9 % slower).
+        if (plan.P == 2 && split_v_built(d) &&
+            table_tiles(max_blocks, block_size) <= kShortTableTiles && 2 * units <= cus)
+            plan.P = 1;
+        // a sequence uses the partitions its length fills: at least 8 tiles
+        // each (none of 16 tiles or fewer splits), or, when the units alone
+        // cover the device, 64 tiles each (none of 128 tiles or fewer splits)
+        plan.part_tiles_log2 = covered ? kLongPartitionTilesLog2 : kMinTilesPerPartitionLog2;
+        plan.solo_tiles = covered ? kLongUnsplitTiles : kUnsplitMaxTiles;
+    } else {
+        plan.P = clamp_partitions(table_tiles(max_blocks, block_size),
+                                  num_partitions < kMaxPartitions ? num_partitions
+                                                                  : kMaxPartitions);
+    }
+    if (plan.P == 1) {
+        // A single pass whose units fill at most half of the compute units
+        // runs as two workgroups per unit, each with half of V's head dim.
+        plan.mode = split_v_built(d) && 2 * units <= cus ? kSingleSplitV : kSingle;
+    } else if (caller_workspace) {
+        plan.mode = kPartials;
+    } else if (num_partitions == 0 && covered) {
+        plan.mode = kFusedLate;  // most partitions of such a launch are empty
+    } else if (split_v_built(d) && 4 * units * plan.P <= cus) {
+        // a split whose workgroups fill at most a quarter of the compute
+        // units also splits V's head dim over two workgroups per partition
+        // (measured: 32 -> 64 workgroups gains ~5 %; 128 -> 256 loses 10-18 %,
+        // the doubled K reads then costing more than the halved V saves)
+        plan.mode = kFusedSplitV;
+    } else {
+        plan.mode = kFused;
+    }
+    return plan;
+}
+
+int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {
     if (B <= 0 || Hkv <= 0 || max_blocks <= 0 || block_size < kTile || num_cus <= 0) return 1;
     const long long units = (long long)B * Hkv;
     const long long tiles = (long long)max_blocks * block_size / kTile;
@@ -291,11 +345,22 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
         return P < kMaxLongSplit ? (int)P : kMaxLongSplit;
     }
     if (tiles <= kUnsplitMaxTiles) return 1;
-    long long P = (num_cus + units - 1) / units;
+    // at most one workgroup per compute unit: a few more would put two on some
+    // units, each taking twice as long as the rest (measured: 96 units, P = 3
+    // is 10-35 % slower than P = 2)
+    long long P = num_cus / units;
     const long long cap = tiles / kMinTilesPerPartition;
     if (P > cap) P = cap;
     if (P > kMaxPartitions) P = kMaxPartitions;
     return clamp_partitions((int)tiles, (int)P);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {
+    return choose_partitions(B, Hkv, max_blocks, block_size, num_cus);
 }
 
 size_t pa_workspace_bytes(int B, int H, int d, int num_partitions) {
@@ -341,38 +406,17 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     hipStream_t s = static_cast<hipStream_t>(stream);
     int dev = 0;
     if ((rc = current_device(&dev)) != PA_OK) return rc;
-    int P;
-    int part_tiles_log2 = 0, solo_tiles = 0;
-    int fused_mode = kFused;
-    if (num_partitions == 0) {
-        const int cus = device_cus(dev);
-        if (cus < 0) return cus;
-        P = pa_choose_partitions(B, Hkv, max_blocks, block_size, cus);
-        // a sequence uses the partitions its length fills: at least 8 tiles
-        // each (none of 16 tiles or fewer splits), or, when the units alone
-        // cover the device, 64 tiles each (none of 128 tiles or fewer splits)
-        const bool covered = (long long)B * Hkv >= cus;
-        part_tiles_log2 = covered ? kLongPartitionTilesLog2 : kMinTilesPerPartitionLog2;
-        solo_tiles = covered ? kLongUnsplitTiles : kUnsplitMaxTiles;
-        // with the units covering the device most partitions are empty
-        if (covered) fused_mode = kFusedLate;
-    } else {
-        P = clamp_partitions(table_tiles(max_blocks, block_size),
-                             num_partitions < kMaxPartitions ? num_partitions : kMaxPartitions);
-    }
+    const int cus = device_cus(dev);
+    if (cus < 0) return cus;
+    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, cus, num_partitions,
+                                workspace != nullptr);
+    const int P = plan.P;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
-    p.part_tiles_log2 = part_tiles_log2;
-    p.solo_tiles = solo_tiles;
+    p.part_tiles_log2 = plan.part_tiles_log2;
+    p.solo_tiles = plan.solo_tiles;
     p.out = out;
-    if (P == 1) {
-        // A single pass whose units fill at most half of the compute units
-        // runs as two workgroups per unit, each with half of V's head dim.
-        const int cus = device_cus(dev);
-        if (cus < 0) return cus;
-        const bool split_v = split_v_built(d) && 2LL * B * Hkv <= cus;
-        return run_main(p, dtype, d, v.G, split_v ? kSingleSplitV : kSingle, s);
-    }
+    if (P == 1) return run_main(p, dtype, d, v.G, plan.mode, s);
     const size_t need = workspace_layout(B, H, P, d).total;
     if (workspace) {
         // caller workspace: split kernel, then the merge kernel (no tickets)
@@ -381,22 +425,27 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         if ((rc = run_main(p, dtype, d, v.G, kPartials, s)) != PA_OK) return rc;
         return run_merge(out, workspace, B, H, P, d, dtype, s);
     }
-    if (fused_mode == kFused && split_v_built(d)) {
-        // a split whose workgroups fill at most a quarter of the compute
-        // units also splits V's head dim over two workgroups per partition
-        // (measured: 32 -> 64 workgroups gains ~5 %; 128 -> 256 loses 10-18 %,
-        // the doubled K reads then costing more than the halved V saves)
-        const int cus = device_cus(dev);
-        if (cus < 0) return cus;
-        if (4LL * B * Hkv * P <= cus) fused_mode = kFusedSplitV;
-    }
     void *ws = nullptr;
     int *tickets = nullptr;
     std::lock_guard<std::mutex> lock(g_mutex);
     if ((rc = library_buffers(dev, s, need, (size_t)B * Hkv, &ws, &tickets)) != PA_OK) return rc;
     attach_workspace(p, ws, d);
     p.counters = tickets;
-    return run_main(p, dtype, d, v.G, fused_mode, s);
+    return run_main(p, dtype, d, v.G, plan.mode, s);
+}
+
+int pa_plan(int B, int Hkv, int d, int max_blocks, int block_size, int num_cus,
+            int num_partitions, int *partitions, int *v_slices_out) {
+    if (!partitions || !v_slices_out) return PA_ERR_NULL;
+    if (B < 0 || Hkv <= 0 || max_blocks <= 0 || num_cus <= 0) return PA_ERR_SHAPE;
+    if (num_partitions < 0) return PA_ERR_VALUE;
+    if (!supported_head_dim(d) || block_size < kTile || block_size > kMaxBlockSize ||
+        (block_size & (block_size - 1)) != 0)
+        return PA_ERR_UNSUPPORTED;
+    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions, false);
+    *partitions = plan.P;
+    *v_slices_out = v_slices(plan.mode);
+    return PA_OK;
 }
 
 int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,

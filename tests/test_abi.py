@@ -62,6 +62,9 @@ def test_strerror_covers_codes():
     (8, 8, 2, 256, 256, 4),       # 512 tokens, 64 units -> 4 partitions of 8 tiles
     (1, 8, 16, 32, 256, 4),       # 512 tokens in 32-token blocks
     (1, 8, 10, 8, 256, 1),        # block_size below 16
+    (12, 8, 64, 16, 256, 2),      # 96 units: floor(256 / 96) = 2, not 3 (no CU holds two)
+    (6, 8, 128, 16, 256, 5),      # 48 units: 5 partitions, 240 workgroups
+    (20, 8, 64, 16, 256, 1),      # 160 units: one partition each
 ])
 def test_choose_partitions(B, Hkv, max_blocks, bs, cus, expect):
     assert pa.pa_choose_partitions(B, Hkv, max_blocks, bs, cus) == expect
@@ -83,8 +86,43 @@ def test_choose_partitions_properties():
                     elif P > 1:
                         # every partition of a full row gets at least 8 tiles
                         assert mb // P >= 8
-                        # and about one workgroup per compute unit, not more
-                        assert B * Hkv * (P - 1) < cus
+                        # and never more workgroups than compute units
+                        assert B * Hkv * P <= cus
+                        # unless the 8-tile floor or the 4096 cap binds, no fewer
+                        # than that either: one more partition would exceed them
+                        assert B * Hkv * (P + 1) > cus or mb // (P + 1) < 8 or P == 4096
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 8, 128, 1024, 16, 256, 0), (32, 1)),   # 16384 tokens: the fused split fills the CUs
+    ((4, 8, 128, 128, 16, 256, 0), (8, 1)),     # 4 x 2048: 256 workgroups
+    ((16, 8, 128, 16, 16, 256, 0), (1, 2)),     # 16 x 256: single pass, 128 units -> V split
+    ((1, 8, 128, 32, 16, 256, 0), (4, 2)),      # 512 tokens: 32 workgroups -> V split
+    ((4, 32, 128, 32, 16, 256, 0), (1, 2)),     # P = 2 on a 32-tile table -> single, V split
+    ((4, 32, 64, 32, 16, 256, 0), (2, 1)),      # ... not for d = 64 (no V split there)
+    ((4, 32, 128, 64, 16, 256, 0), (2, 1)),     # ... nor for a 64-tile table
+    ((40, 8, 128, 256, 16, 256, 0), (4, 1)),    # units cover the device
+    ((40, 8, 128, 256, 16, 256, 1), (1, 1)),    # forced single pass, 320 units: no V split
+    ((2, 8, 128, 4, 16, 256, 1), (1, 2)),       # forced single pass, 16 units: V split
+    ((2, 8, 128, 64, 16, 256, 3), (3, 2)),      # forced split, 48 workgroups: V split
+    ((2, 8, 128, 64, 16, 256, 5), (5, 1)),      # forced split, 80 workgroups: no V split
+    ((2, 8, 256, 64, 16, 256, 3), (3, 2)),
+    ((0, 8, 128, 64, 16, 256, 0), (1, 2)),
+])
+def test_plan(args, expect):
+    assert pa.pa_plan(*args) == expect
+
+
+def test_plan_rejects_bad_arguments():
+    lib = pa.load()
+    import ctypes
+    P, vs = ctypes.c_int(), ctypes.c_int()
+    assert lib.pa_plan(1, 8, 128, 4, 16, 256, 0, None, ctypes.byref(vs)) == pa.PA_ERR_NULL
+    bad = [((1, 0, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 0, 0), pa.PA_ERR_SHAPE),
+           ((-1, 8, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 256, -1), pa.PA_ERR_VALUE),
+           ((1, 8, 96, 4, 16, 256, 0), pa.PA_ERR_UNSUPPORTED), ((1, 8, 128, 4, 8, 256, 0), pa.PA_ERR_UNSUPPORTED)]
+    for a, code in bad:
+        assert lib.pa_plan(*a, ctypes.byref(P), ctypes.byref(vs)) == code, a
 
 
 def test_workspace_bytes():
