@@ -57,6 +57,12 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--case", default=None, metavar="B,CTX,H,HKV,D,BS,DTYPE",
+                    help="time this shape instead of a named workload (uniform context "
+                         "length CTX, a scattered table over exactly the blocks needed, "
+                         "DTYPE bf16|f16|f32); implies --no-per-config")
+    ap.add_argument("--partitions", type=int, default=0,
+                    help="partition count for the timed workload (0 = the heuristic)")
     ap.add_argument("--variant", default=None, choices=["valu_qk"],
                     help="time an ablation build instead of the library: valu_qk runs the "
                          "q.K product on the vector ALUs instead of the matrix cores")
@@ -262,10 +268,8 @@ def recorded_traffic(workload_name):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cid, budget_s):
+def cpu_baseline(case, budget_s):
     import oracle
-    import pa_inputs as pi
-    case = pi.make_config_case(cid)
     threads = oracle.max_threads()
     oracle.decode_case(case, threads=threads)  # load, first touch
     reps, t0 = 0, time.perf_counter()
@@ -278,7 +282,7 @@ def cpu_baseline(cid, budget_s):
     per = el / reps
     return dict(value=round(case.algorithmic_bytes() / per / 1e9, 4), unit="GB/s",
                 cores=threads, kind="oracle",
-                sample=f"the full workload-{cid} step ({case.name}), {reps} repetitions, "
+                sample=f"the full step of {case.name}, {reps} repetitions, "
                        f"{per * 1e3:.1f} ms each, fp64 C oracle with OpenMP over (b, h)",
                 ms_per_step=round(per * 1e3, 3))
 
@@ -455,8 +459,15 @@ def main():
         print(json.dumps(fn(dev, min(args.steps, 500), args.warmup, use_graph)), flush=True)
         return
 
+    if args.case:
+        B, ctx, H, Hkv, d, bs, dt = args.case.split(",")
+        B, ctx, H, Hkv, d, bs = (int(x) for x in (B, ctx, H, Hkv, d, bs))
+        headline = pi.make_case(B, ctx, H, Hkv, d, bs, dtype=dt, seed=B * 1000 + ctx,
+                                name=f"{dt} B={B} ctx={ctx} H={H} Hkv={Hkv} d={d} bs={bs}")
+    else:
+        headline = pi.make_config_case(args.workload)
     per_config = []
-    if not args.no_per_config:
+    if not args.no_per_config and not args.case:
         plan = [(c, 0) for c in (1, 2, 3, 4, 5) if c != args.workload] + [(4, 1), (5, 1)]
         for cid, parts in plan:
             w, ts, err = measure(pi.make_config_case(cid), dev, min(args.steps, 1000),
@@ -474,10 +485,9 @@ def main():
             del w
             torch.cuda.empty_cache()
 
-    w, t_step, err = measure(pi.make_config_case(args.workload), dev, args.steps, args.warmup,
-                             use_graph)
+    w, t_step, err = measure(headline, dev, args.steps, args.warmup, use_graph, args.partitions)
     gbs = w.bytes / t_step / 1e9
-    log(f"headline workload {args.workload} P={w.P}: {t_step * 1e6:.2f} us/step {gbs:.0f} GB/s")
+    log(f"timed workload {headline.name} P={w.P}: {t_step * 1e6:.2f} us/step {gbs:.0f} GB/s")
     if not w.single_launch():
         raise SystemExit("the headline step must be a single kernel launch")
     # the step is one launch of the dominant kernel: its timed region is the step's
@@ -495,7 +505,7 @@ def main():
 
     base = None
     if args.cpu_seconds > 0:
-        base = cpu_baseline(args.workload, args.cpu_seconds)
+        base = cpu_baseline(headline, args.cpu_seconds)
 
     line = {
         "metric": METRIC,

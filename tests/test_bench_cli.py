@@ -19,10 +19,12 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_cpu_baseline_fields():
-    base = bench.cpu_baseline(1, 0.2)
+    import pa_inputs as pi
+    case = pi.make_config_case(1)
+    base = bench.cpu_baseline(case, 0.2)
     assert base["kind"] == "oracle" and base["unit"] == "GB/s"
     assert base["value"] > 0 and base["cores"] >= 1 and base["ms_per_step"] > 0
-    assert "workload-1" in base["sample"]
+    assert case.name in base["sample"]
 
 
 def test_recorded_traffic_needs_matching_workload():
