@@ -8,7 +8,9 @@
 //
 // * One workgroup per (kvh, b[, partition]) serves all G = H / Hkv query heads
 //   of the group, so each K/V row is read from HBM once per kv head, not once
-//   per query head.
+//   per query head.  (A launch too small to fill the device gives each unit or
+//   partition two workgroups, one per half of V's head dim; both read K, the
+//   second mostly from the XCD's L2.)
 // * A wave consumes 16-token tiles, two in flight at a time (one group); a
 //   sequence's tiles are dealt in runs of 2 to the 4 * busy (partition, wave)
 //   lanes in turn, busy being the partitions its length fills.  Block
