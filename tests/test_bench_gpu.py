@@ -39,3 +39,22 @@ def test_bench_prints_one_consistent_json_line(gpu):
     assert r["bytes_per_launch"] == bytes_per_step
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+
+
+def test_bench_case_option_reports_its_launch(gpu):
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--case",
+           "2,300,32,8,128,16,f16", "--partitions", "3", "--cpu-seconds", "0",
+           "--steps", "50", "--warmup", "3"]
+    print("bench.py --case 2,300,32,8,128,16,f16 --partitions 3", flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=110, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [l for l in res.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, res.stdout
+    d = json.loads(lines[0])
+    c = d["config"]
+    assert d["dtype"] == "f16" and c["batch"] == 2 and c["context_len"] == 300
+    assert c["num_heads"] == 32 and c["num_kv_heads"] == 8 and c["block_size"] == 16
+    # 16 units x 3 partitions fill at most a quarter of the CUs: V split in two
+    assert c["num_partitions"] == 3 and c["v_slices"] == 2
+    assert d["per_config"] == [] and d["cpu_baseline"] is None
+    assert d["roofline"]["traffic"] is None   # counters were taken on another workload
