@@ -236,6 +236,22 @@ def test_long_context_many_chunks(gpu, dtype, parts):
     assert_close(to_f64(out), ref, dtype, f"long P={parts}")
 
 
+def test_maximum_table_width(gpu):
+    # the widest table the library takes: 2^22 entries of 256-token blocks
+    # (2^30 tokens per row); one sequence of 2^20 tokens and a short one, so
+    # that tile counts, partition deals and offsets run near their limits
+    B, bs, W = 2, 256, 1 << 22
+    lens = [1 << 20, 300]
+    case = pi.make_case(B, lens, 2, 1, 64, bs, dtype="bf16", seed=17, max_blocks=W,
+                        pool=sum(math.ceil(n / bs) for n in lens) + 1)
+    assert case.max_blocks * case.block_size == 1 << 30
+    ref = oracle.decode_case(case)
+    for parts in (0, 1, 4096):
+        say(f"table width 2^22 x 256 tokens, lengths {lens}, P={parts}")
+        out = run_gpu(case, gpu, num_partitions=parts)
+        assert_close(to_f64(out), ref, "bf16", f"max width P={parts}")
+
+
 def test_graph_replay_matches_eager(gpu):
     # the fused split path (tickets in the library workspace) captured into a
     # graph: every replay, with eager work between replays, equals eager
