@@ -252,6 +252,44 @@ def test_maximum_table_width(gpu):
         assert_close(to_f64(out), ref, "bf16", f"max width P={parts}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("scale", [4.0, -4.0, 0.0])
+def test_extreme_score_ranges(gpu, dtype, scale):
+    # scores spread over tens to hundreds (log2 units) move the reference max
+    # many times and give the partitions of a split very different maxima;
+    # scale 0 makes every score equal.  Ragged lengths, a hole; heuristic,
+    # single pass and forced splits.
+    # The stated tolerances hold at the workloads' scale.  Here the scores'
+    # own fp32 rounding grows with them: the q.K accumulation over d terms
+    # errs by at most gamma_d * sum_i |q_i K_i| <= gamma_d * |q| |K| (Cauchy-
+    # Schwarz; gamma_d = d u / (1 - d u), u = 2^-24; plus two roundings for
+    # the scale), in log2 units times |scale log2 e|, and the softmax passes a
+    # score error ds to the output as at most ln2 * ds * 2 max|V|.  That bound
+    # is added to the tolerance; a wrong rescale would be off by O(1).
+    base = pi.make_case(3, [1500, 37, 700], 32, 8, 128, 16, dtype=dtype, seed=18,
+                        holes=[(0, 20)])
+    case = pi.Case(**{f: getattr(base, f) for f in base.__dataclass_fields__})
+    case.scale = np.float32(scale)
+    ref = oracle.decode_case(case)
+    u, d = 2.0 ** -24, case.head_dim
+    gamma = d * u / (1 - d * u)
+    qn = np.linalg.norm(case.q.astype(np.float64), axis=-1).max()
+    kn = np.linalg.norm(case.k_cache.astype(np.float64), axis=-1).max()
+    ds = abs(float(case.scale)) * 1.4426950408889634 * (gamma + 2 * u) * qn * kn
+    extra = np.log(2.0) * ds * 2 * np.abs(case.v_cache).max()
+    for parts in (0, 1, 5, 33):
+        say(f"scale {scale} {dtype} P={parts} (score rounding allowance {extra:.2e})")
+        got = to_f64(run_gpu(case, gpu, num_partitions=parts))
+        err = np.abs(got - ref)
+        atol, rtol = {"f32": (1e-5, 0.0), "bf16": (2e-3, 1e-2),
+                      "f16": (5e-5, 2.0 ** -10)}[dtype]
+        assert np.isfinite(got).all()
+        bad = err > atol + extra + rtol * np.abs(ref)
+        assert not bad.any(), (f"scale {scale} P={parts}: {bad.sum()} out of tolerance, "
+                               f"max err {err.max():.3e}, allowance {extra:.3e}")
+        say(f"  max abs err {err.max():.3e}")
+
+
 def test_graph_replay_matches_eager(gpu):
     # the fused split path (tickets in the library workspace) captured into a
     # graph: every replay, with eager work between replays, equals eager
