@@ -54,6 +54,9 @@
  *     table entry inside the context (-1) removes that block's tokens from
  *     the softmax; every other entry used must be a valid pool block.  A
  *     sequence with no live token gets an all-zero output row.
+ *   - Range: scores and sums are fp32, so inputs must keep them finite there.
+ *     |scale * q . K| finite in fp32 and |V| < 2^90 suffice, since softmax
+ *     weights up to 2^8 are summed over at most 2^30 tokens.
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H
