@@ -215,6 +215,39 @@ def test_non_default_stream(gpu):
     assert_close(to_f64(out), oracle.decode_case(case), "bf16", "side stream")
 
 
+def test_decode_helper(gpu):
+    # the tensor-level helper: shapes from the tensors, out allocated or given,
+    # a forced count, a caller workspace tensor and the pool guard, all to the
+    # same result within tolerance; wrong arguments are refused before a launch
+    case = pi.make_case(3, [700, 1, 260], 32, 8, 128, 16, dtype="bf16", seed=19,
+                        holes=[(0, 7)])
+    d = DeviceCase(case, gpu)
+    ref = oracle.decode_case(case)
+    say("decode() helper")
+    out = pa.decode(d.q, d.k, d.v, d.table, d.lens, float(case.scale))
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), ref, "bf16", "decode() heuristic")
+    given = torch.empty_like(d.q)
+    same = pa.decode(d.q, d.k, d.v, d.table, d.lens, float(case.scale), out=given,
+                     num_partitions=1, num_pool_blocks=case.num_pool_blocks)
+    torch.cuda.synchronize()
+    assert same is given
+    assert_close(to_f64(given), ref, "bf16", "decode() single pass, pool guard")
+    nbytes = pa.pa_workspace_bytes(case.batch, case.num_heads, case.head_dim, 5)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    split = pa.decode(d.q, d.k, d.v, d.table, d.lens, float(case.scale), num_partitions=5,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(to_f64(split), ref, "bf16", "decode() caller workspace")
+    with pytest.raises(pa.PaError):
+        pa.decode(d.q, d.k, d.v, d.table.long(), d.lens, float(case.scale))
+    with pytest.raises(pa.PaError):
+        pa.decode(d.q.transpose(0, 1), d.k, d.v, d.table, d.lens, float(case.scale))
+    with pytest.raises(pa.PaError):
+        pa.decode(d.q, d.k, d.v, d.table, d.lens, float(case.scale), num_partitions=5,
+                  workspace=ws[:16])
+
+
 def test_empty_batch_launches_nothing(gpu):
     q = torch.empty(0, 32, 128, dtype=torch.bfloat16, device=gpu)
     k = torch.empty(4, 16, 8, 128, dtype=torch.bfloat16, device=gpu)
