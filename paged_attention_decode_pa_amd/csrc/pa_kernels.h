@@ -943,17 +943,30 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
-        // Publish this partition (its coherent stores complete before the
-        // barrier), take a ticket; the last of the VS * `busy` workgroups of
-        // (b, kvh) merges their partitions and resets the ticket for the next
-        // call.
+        // Publish this partition and take a ticket; the last of the VS * `busy`
+        // workgroups of (b, kvh) merges their partitions and resets the ticket
+        // for the next call.  Ordering, in the memory model's terms: every
+        // thread's partial stores are sequenced before the barrier, which
+        // synchronises the workgroup (workgroup scope) with thread 0; thread
+        // 0's ticket is an agent-scope release read-modify-write, so the
+        // stores of all threads happen before it.  The tickets of one (b, kvh)
+        // form a release sequence, so in the workgroup whose ticket reads
+        // VS * busy - 1 the agent-scope acquire fence that follows makes every
+        // earlier ticket -- and so every other workgroup's stores -- happen
+        // before it, and through the second barrier before every thread's
+        // merge loads.  Only the merging workgroup pays for the acquire (an
+        // invalidate of its caches).  (The waitcnt lets each wave's stores
+        // complete before the barrier, so the release has little left to wait
+        // for.)
         __shared__ int sm_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
             const int prev = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sm_last = prev == VS * busy - 1;
+                                                    __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = prev == VS * busy - 1;
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            sm_last = last;
         }
         __syncthreads();
         if (sm_last) {
