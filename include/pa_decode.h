@@ -34,10 +34,13 @@
  * Conventions:
  *   - Supported shapes: d in {64, 128, 256} (the benchmark script's head_dim
  *     argument; 128 in every configuration of the docs page); block_size a
- *     power of two from 16 to 256;
- *     H % Hkv == 0 with H / Hkv in {1, 2, 4, 8, 16}; B * H < 2^31;
- *     max_blocks * block_size <= 2^30.  Others return PA_ERR_UNSUPPORTED.  Sequences are processed in tiles of 16 tokens; a
- *     row of the table covers T = max_blocks * block_size / 16 tiles.
+ *     power of two from 16 to 256; H % Hkv == 0 with G = H / Hkv in
+ *     {1, 2, 4, 8, 16}, except that d = 256 is built only for G <= 8 with
+ *     bf16 and fp16 and for G <= 2 with fp32 (the fp32 accumulators of the
+ *     other d = 256 groups would not fit the register file); B * H < 2^31;
+ *     max_blocks * block_size <= 2^30.  Others return PA_ERR_UNSUPPORTED.
+ *     Sequences are processed in tiles of 16 tokens; a row of the table
+ *     covers T = max_blocks * block_size / 16 tiles.
  *   - All calls only enqueue work on `stream` (a hipStream_t, NULL = the null
  *     stream); nothing synchronises with the host.  The return code reports
  *     errors the host can see: argument validation (checked before any HIP
@@ -199,7 +202,11 @@ int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, 
 size_t pa_workspace_bytes(int B, int H, int d, int num_partitions);
 
 /*
- * The launch heuristic (pure; no HIP call).  Work units are the B * Hkv
+ * The launch heuristic (pure; no HIP call).  The flash-decoding-bench design
+ * note, implementations section, picks the chunk size of its split from the
+ * KV length, trading loop overhead against parallelism; here the partition
+ * count follows the table width and how many (sequence, kv head) units the
+ * device's compute units can take.  Work units are the B * Hkv
  * (sequence, kv-head) pairs; each is one workgroup in a single pass.  When
  * they are fewer than num_cus it splits the W = max_blocks * block_size / 16
  * tiles of a table row into floor(num_cus / units) partitions, so that the
@@ -215,7 +222,9 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
 
 /*
  * The launch pa_decode_ex makes for these sizes on a device of num_cus compute
- * units when no caller workspace is given (pure; no HIP call): *partitions =
+ * units when no caller workspace is given (pure; no HIP call), i.e. the
+ * length-based choice of the split (flash-decoding-bench design note,
+ * implementations section) as pa_decode applies it: *partitions =
  * the context partition count P it uses (num_partitions as in pa_decode_ex:
  * 0 = heuristic, n > 0 = forced), *v_slices = 2 when each unit (P == 1) or
  * each partition (P > 1) is served by two workgroups, one per half of V's

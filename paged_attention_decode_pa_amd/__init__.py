@@ -194,25 +194,50 @@ def pa_release() -> None:
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, out=None, stream=None,
-           num_partitions=0, num_pool_blocks=0, workspace=None):
+           num_partitions=0, num_pool_blocks=None, workspace=None):
     """Tensor-level convenience: shapes are read from the tensors, ``out`` is
-    allocated with torch when not given, and the call goes to pa_decode_ex."""
+    allocated with torch when not given, and the call goes to pa_decode_ex.
+    ``num_pool_blocks`` defaults to ``k_cache.shape[0]``, so table entries past
+    the pool are skipped like -1 instead of being read.  Every check below runs
+    before anything is launched: the C side sees only pointers, so a pool of
+    another head dim or a short ``out`` would otherwise be read or written out
+    of bounds."""
     import torch
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise PaError(PA_ERR_SHAPE, "q must be [B][H][d] and k_cache [pool][block_size][Hkv][d]")
     B, H, d = q.shape
-    _, block_size, Hkv, _ = k_cache.shape
-    max_blocks = block_tables.shape[1]
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_tables", block_tables), ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise PaError(PA_ERR_SHAPE, f"{name} must be contiguous")
-        if not t.is_cuda or t.device != q.device:
-            raise PaError(PA_ERR_DEVICE, f"{name} must be on q's GPU")
+    _, block_size, Hkv, kd = k_cache.shape
+    if kd != d:
+        raise PaError(PA_ERR_SHAPE, f"k_cache head dim {kd} != q head dim {d}")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise PaError(PA_ERR_SHAPE, "v_cache must have k_cache's shape")
+    if (block_tables.dim() != 2 or block_tables.shape[0] != B
+            or tuple(context_lens.shape) != (B,)):
+        raise PaError(PA_ERR_SHAPE, "block_tables must be [B][max_blocks], context_lens [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise PaError(PA_ERR_DTYPE, "q, k_cache and v_cache must share a dtype")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise PaError(PA_ERR_DTYPE, "block_tables and context_lens must be int32")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or v_cache.shape != k_cache.shape:
-        raise PaError(PA_ERR_DTYPE, "q, k_cache and v_cache must share dtype and shape")
-    if tuple(context_lens.shape) != (B,) or block_tables.shape[0] != B:
-        raise PaError(PA_ERR_SHAPE, "block_tables must be [B][max_blocks], context_lens [B]")
+    if out is not None:
+        if tuple(out.shape) != tuple(q.shape):
+            raise PaError(PA_ERR_SHAPE, f"out has shape {tuple(out.shape)}, q {tuple(q.shape)}")
+        if out.dtype != q.dtype:
+            raise PaError(PA_ERR_DTYPE, "out must have q's dtype")
+    tensors = [("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+               ("block_tables", block_tables), ("context_lens", context_lens)]
+    if out is not None:
+        tensors.append(("out", out))
+    if workspace is not None:
+        tensors.append(("workspace", workspace))
+    for name, t in tensors:
+        if not t.is_contiguous():
+            raise PaError(PA_ERR_SHAPE, f"{name} must be contiguous")
+    for name, t in tensors:
+        if not t.is_cuda or t.device != q.device:
+            raise PaError(PA_ERR_DEVICE, f"{name} must be on q's GPU")
+    max_blocks = block_tables.shape[1]
+    if num_pool_blocks is None:
+        num_pool_blocks = k_cache.shape[0]
     if out is None:
         out = torch.empty_like(q)
     ws_bytes = 0

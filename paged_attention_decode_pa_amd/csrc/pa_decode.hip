@@ -377,7 +377,8 @@ const char *pa_strerror(int code) {
         case PA_ERR_SHAPE: return "negative or inconsistent sizes";
         case PA_ERR_UNSUPPORTED:
             return "shape not supported (needs d in {64,128,256}, block_size a power of 2 in "
-                   "16..256, H/Hkv in {1,2,4,8,16})";
+                   "16..256, H/Hkv in {1,2,4,8,16}; d=256 only with H/Hkv <= 8 for bf16/fp16 "
+                   "and <= 2 for fp32)";
         case PA_ERR_DTYPE: return "unknown dtype";
         case PA_ERR_ALIGN: return "pointer alignment (16 bytes for tensors, 4 for int32 arrays)";
         case PA_ERR_WORKSPACE:

@@ -251,3 +251,47 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(pa.PaError):
         pa.dtype_code(torch.float64)
     assert pa.dtype_code(torch.float16) == pa.PA_DTYPE_F16
+
+
+def test_decode_helper_refuses_mismatched_tensors_before_any_launch():
+    # the C side sees only pointers: a pool of another head dim, a short or
+    # mistyped `out` or a strided workspace would be read or written out of
+    # bounds, so decode() refuses each of them itself.  On this host every
+    # tensor is a CPU tensor, so each refusal below (a shape or dtype code, not
+    # PA_ERR_DEVICE) shows that the check runs before the device check and
+    # hence before anything is handed to the library.
+    import torch
+    B, H, Hkv, d, bs = 2, 32, 8, 128, 16
+    q = torch.zeros(B, H, d, dtype=torch.bfloat16)
+    k = torch.zeros(4, bs, Hkv, d, dtype=torch.bfloat16)
+    t = torch.zeros(B, 2, dtype=torch.int32)
+    n = torch.zeros(B, dtype=torch.int32)
+
+    def code(**kw):
+        args = dict(q=q, k_cache=k, v_cache=k, block_tables=t, context_lens=n)
+        extra = {key: kw.pop(key) for key in ("out", "workspace") if key in kw}
+        args.update(kw)
+        with pytest.raises(pa.PaError) as e:
+            pa.decode(args["q"], args["k_cache"], args["v_cache"], args["block_tables"],
+                      args["context_lens"], 0.1, **extra)
+        return e.value.code
+
+    k64 = torch.zeros(4, bs, Hkv, 64, dtype=torch.bfloat16)
+    assert code(k_cache=k64, v_cache=k64) == pa.PA_ERR_SHAPE          # head dim differs
+    assert code(v_cache=torch.zeros(5, bs, Hkv, d, dtype=torch.bfloat16)) == pa.PA_ERR_SHAPE
+    assert code(q=q[0]) == pa.PA_ERR_SHAPE                             # not [B][H][d]
+    assert code(block_tables=torch.zeros(B + 1, 2, dtype=torch.int32)) == pa.PA_ERR_SHAPE
+    assert code(context_lens=torch.zeros(B + 1, dtype=torch.int32)) == pa.PA_ERR_SHAPE
+    assert code(out=torch.zeros(B, H, d - 2, dtype=torch.bfloat16)) == pa.PA_ERR_SHAPE
+    assert code(out=torch.zeros(B - 1, H, d, dtype=torch.bfloat16)) == pa.PA_ERR_SHAPE
+    assert code(out=torch.zeros(B, H, d, dtype=torch.float16)) == pa.PA_ERR_DTYPE
+    assert code(out=torch.zeros(H, B, d, dtype=torch.bfloat16).transpose(0, 1)) == \
+        pa.PA_ERR_SHAPE                                                # not contiguous
+    strided_ws = torch.zeros(64, 2, dtype=torch.uint8)[:, 0]
+    assert code(workspace=strided_ws) == pa.PA_ERR_SHAPE
+    assert code(k_cache=k.float(), v_cache=k.float()) == pa.PA_ERR_DTYPE
+    assert code(block_tables=t.long()) == pa.PA_ERR_DTYPE
+    # every shape right: only then the device check (host tensors refused)
+    assert code() == pa.PA_ERR_DEVICE
+    assert code(out=torch.zeros(B, H, d, dtype=torch.bfloat16),
+                workspace=torch.zeros(64, dtype=torch.uint8)) == pa.PA_ERR_DEVICE
