@@ -9,19 +9,26 @@ library's heuristic.
 Timing: inputs are resident in HBM before the timed region.  Each step uses
 the next of N distinct copies of (K/V pool, q, table, lengths, out), N chosen
 so the copies span >= 1 GiB, so the 256 MB Infinity Cache cannot serve a
-step's K/V reads from the previous visit.  W warm-up steps, then exactly K
-steps between two synchronisations, recorded by HIP events on the stream the
-kernels run on.  By default the K steps are replayed from one HIP graph
-(capture of the same K pa_decode calls) so host launch overhead does not set
-the pace; --eager times plain launches.
+step's K/V reads from the previous visit.  W warm-up steps, then REPS (5)
+timed regions of exactly K steps each, recorded by HIP events on the stream
+the kernels run on.  The K steps are captured in HIP graphs (--eager times
+plain launches); an untimed region is enqueued first and the regions follow
+back to back with no host synchronisation between them, so the GPU is busy
+when every start event fires and no launch gap lands inside a region.  The
+rotation runs on across the regions (one graph per starting copy).  value is
+the median region; the minimum is reported beside it.
 
 Output: one JSON line (rank 0, N = 1).  value = algorithmic bytes per step /
 step time (GB/s); algorithmic bytes = every live K and V row once per kv head
 + q + out + block table.  A step of the headline workload is one launch of
 the split kernel with its fused merge, so "roofline" (the dominant kernel)
-uses the same timed region: algorithmic bytes per launch / average launch
-time.  "cpu_baseline" times the fp64 C oracle on the host's cores on the same
-workload.  "per_config" adds the other workloads and the single-pass runs.
+uses the same timed regions: algorithmic bytes per launch / average launch
+time.  Beside it the roofline reports the read ceiling: a plain streaming
+read of the same bytes with the kernel's load shape (libpa_read_probe.so),
+timed the same way.  "cpu_baseline" times the fp64 C oracle on the host's
+cores (and on one) on the same workload.  "per_config" adds the other
+workloads and the single-pass runs, each measured in a child process of its
+own, so that a fault in one is reported as that configuration's CRASH.
 """
 import argparse
 import json
@@ -40,6 +47,7 @@ METRIC = "decode step μs and achieved HBM GB/s (% of MI355X peak) per config"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATION_BYTES = 1 << 30       # distinct bytes the copies must span
 MAX_COPIES = 64
+REPS = 5                       # timed regions of K steps; the median is reported
 VARIANT = None                 # ablation library to time instead (--variant)
 
 
@@ -68,6 +76,12 @@ def parse():
                          "q.K product on the vector ALUs instead of the matrix cores")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (counter scale)")
+    ap.add_argument("--reps", type=int, default=REPS,
+                    help="timed regions of --steps steps each (median reported)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain streaming-read leg")
+    ap.add_argument("--leg", default=None, metavar="WORKLOAD:PARTITIONS",
+                    help=argparse.SUPPRESS)   # one per-config leg, run as a child process
     ap.add_argument("--sweep", nargs="?", const="design-note", default=None,
                     choices=["design-note", "ragged", "script", "shapes"],
                     help="instead of the headline, a sweep: design-note (single pass vs split "
@@ -82,6 +96,12 @@ TORCH_DTYPES = {"bf16": "bfloat16", "f16": "float16", "f32": "float32"}
 TOLERANCE = {"f32": (1e-5, 0.0), "bf16": (2e-3, 1e-2), "f16": (5e-5, 2.0 ** -10)}
 
 
+def rotation_copies(step_bytes):
+    """Distinct input copies one workload rotates over: enough to span
+    ROTATION_BYTES, at most MAX_COPIES, at least 2."""
+    return max(2, min(MAX_COPIES, math.ceil(ROTATION_BYTES / step_bytes)))
+
+
 class Workload:
     """N rotation copies of one workload's inputs on the device."""
 
@@ -92,7 +112,7 @@ class Workload:
         self.case = case
         c = self.case
         self.bytes = c.algorithmic_bytes()
-        self.ncopies = max(2, min(MAX_COPIES, math.ceil(ROTATION_BYTES / self.bytes)))
+        self.ncopies = rotation_copies(self.bytes)
         if c.dtype != "f32":
             tdt = getattr(torch, TORCH_DTYPES[c.dtype])
             conv = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(tdt)
@@ -114,6 +134,8 @@ class Workload:
         self.P, self.v_slices = pa.pa_plan(c.batch, c.num_kv_heads, c.head_dim, c.max_blocks,
                                            c.block_size, self.cus, num_partitions)
         self.num_partitions = num_partitions
+        # every step here uses the library-owned workspace (no caller workspace)
+        self.caller_workspace = False
         self.lib = pa.load_variant(VARIANT) if VARIANT else pa.load()
 
     def step(self, i, stream):
@@ -134,10 +156,16 @@ class Workload:
         if rc != 0:
             raise RuntimeError(f"pa_decode failed: {rc}")
 
+    def launches_per_step(self):
+        """Kernel launches of one step, from the plan: the single pass is one;
+        a split is one with the library workspace (fused merge), two with a
+        caller workspace (split kernel, then merge kernel)."""
+        if self.P == 1 or not self.caller_workspace:
+            return 1
+        return 2
+
     def single_launch(self):
-        """True when one step is one kernel launch: the single pass, or the
-        fused split (every step here uses the library-owned workspace)."""
-        return True
+        return self.launches_per_step() == 1
 
     def kernel_name(self):
         v = ", V split in two" if self.v_slices > 1 else ""
@@ -146,46 +174,67 @@ class Workload:
         return f"pa_decode_kernel (split, fused merge{v})"
 
 
-def time_region(fn, steps, warmup, use_graph):
-    """Seconds per call of fn(i, stream) over exactly `steps` calls."""
+def time_region(fn, steps, warmup, use_graph, ncopies, reps=REPS):
+    """Seconds per call of fn(i, stream) in each of `reps` regions of exactly
+    `steps` calls.  Call i uses rotation copy i % ncopies; an untimed region
+    goes first and the timed ones follow back to back on one stream with no
+    host synchronisation in between, and the call index runs on across them,
+    so every region starts on a busy GPU and continues the rotation."""
     import torch
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
     if use_graph:
-        # warm up on the capture stream itself: the library keeps its split
-        # workspace per stream and must not allocate while capturing
-        g = torch.cuda.CUDAGraph()
+        # one graph per starting copy the regions need: region r starts at
+        # call r * steps, i.e. at copy (r * steps) % ncopies
+        ngraphs = ncopies // math.gcd(ncopies, steps)
+        graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
+        # warm up on the capture stream itself: the library keeps its split
+        # workspace per stream and must not allocate while capturing
         with torch.cuda.stream(cap):
             for i in range(warmup):
                 fn(i, cap.cuda_stream)
         torch.cuda.synchronize()
-        with torch.cuda.stream(cap):
-            g.capture_begin()
-            for i in range(steps):
-                fn(i, cap.cuda_stream)
-            g.capture_end()
+        for gi in range(ngraphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                g.capture_begin()
+                for i in range(steps):
+                    fn(gi * steps + i, cap.cuda_stream)
+                g.capture_end()
+            graphs.append(g)
         torch.cuda.synchronize()
-        g.replay()          # one untimed replay
+        graphs[0].replay()                 # untimed region 0
+        for r, (start, end) in enumerate(events):
+            start.record(stream)
+            graphs[(r + 1) % ngraphs].replay()
+            end.record(stream)
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        del g
+        del graphs
     else:
         for i in range(warmup):
             fn(i, sh)
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for i in range(steps):
+        for i in range(steps):             # untimed region 0
             fn(i, sh)
-        end.record(stream)
+        for r, (start, end) in enumerate(events):
+            start.record(stream)
+            for i in range(steps):
+                fn((r + 1) * steps + i, sh)
+            end.record(stream)
         torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3 / steps
+    return [a.elapsed_time(b) * 1e-3 / steps for a, b in events]
+
+
+def summarize(times):
+    """(median, min) of per-region seconds per step."""
+    t = sorted(times)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return med, t[0]
 
 
 def parity_gate(w):
@@ -202,7 +251,9 @@ def parity_gate(w):
     return ok and same, float(err.max())
 
 
-def measure(case, dev, steps, warmup, use_graph, num_partitions=0):
+def measure(case, dev, steps, warmup, use_graph, num_partitions=0, reps=REPS):
+    """The workload's parity gate, then its timed regions: (Workload, median
+    seconds per step, min seconds per step, max abs error)."""
     w = Workload(case, dev, num_partitions)
     for i in range(w.ncopies):
         w.step(i, None)
@@ -210,8 +261,39 @@ def measure(case, dev, steps, warmup, use_graph, num_partitions=0):
     if not ok:
         raise SystemExit(f"{case.name}: parity gate FAILED (max err {max_err:.3e}); "
                          "timing would be meaningless")
-    t_step = time_region(w.step, steps, warmup, use_graph)
-    return w, t_step, max_err
+    med, best = summarize(time_region(w.step, steps, warmup, use_graph, w.ncopies, reps))
+    return w, med, best, max_err
+
+
+def read_ceiling(dev, nbytes, workgroups, steps, warmup, use_graph, reps=REPS):
+    """Seconds per launch of a plain streaming read of nbytes (rounded up to
+    16 bytes) with the decode kernel's load shape: `workgroups` workgroups of 4
+    waves, 16 KB of non-temporal 16-byte loads in flight per wave, over a
+    rotation of copies spanning >= 1 GiB like the decode step's."""
+    import ctypes
+    import torch
+    from paged_attention_decode_pa_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        raise RuntimeError(f"{hip_build.PROBE_LIB} not found: build the package first")
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_probe_read.restype = ctypes.c_int
+    nbytes = (nbytes + 15) // 16 * 16
+    ncopies = rotation_copies(nbytes)
+    bufs = [torch.zeros(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(ncopies)]
+    sink = torch.zeros(workgroups, dtype=torch.int32, device=dev)
+
+    def fn(i, stream):
+        rc = lib.pa_probe_read(bufs[i % ncopies].data_ptr(), nbytes, workgroups, 16,
+                               sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"pa_probe_read failed: {rc}")
+
+    med, best = summarize(time_region(fn, steps, warmup, use_graph, ncopies, reps))
+    del bufs
+    torch.cuda.empty_cache()
+    return med, best, nbytes
 
 
 def strip_c_comments(text):
@@ -268,23 +350,74 @@ def recorded_traffic(workload_name):
     return int(rec["traffic_bytes_per_launch"])
 
 
+def cpu_description():
+    """The host's CPU model and core counts, from /proc/cpuinfo and the
+    process's affinity mask."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8", errors="replace"):
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name" and model is None:
+                model = val
+            elif key == "physical id":
+                phys = val
+            elif key == "core id":
+                core = val
+            elif not key:
+                if core is not None:
+                    cores.add((phys, core))
+                phys = core = None
+        if core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return dict(cpu_model=model, physical_cores=len(cores) or None,
+                logical_cpus=os.cpu_count(), usable_cpus=usable)
+
+
+def time_oracle(case, threads, budget_s):
+    """Median seconds per full step of the oracle on `threads` OpenMP threads
+    over repetitions filling about budget_s (at least 5, or 1 if one alone
+    takes longer than the budget), and the repetition count."""
+    import oracle
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_case(case, threads=threads)
+        times.append(time.perf_counter() - t0)
+        el = time.perf_counter() - t_all
+        if len(times) >= 5 and el >= budget_s:
+            break
+        if el * (len(times) + 1) / len(times) > 3 * budget_s:
+            break
+    med, _ = summarize(times)
+    return med, len(times)
+
+
 def cpu_baseline(case, budget_s):
+    """The fp64 C oracle on the same workload: on all the threads OpenMP
+    takes (the reported value) and on one thread."""
     import oracle
     threads = oracle.max_threads()
     oracle.decode_case(case, threads=threads)  # load, first touch
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_case(case, threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or (reps >= 1 and el * (reps + 1) / reps > 3 * budget_s):
-            break
-    per = el / reps
-    return dict(value=round(case.algorithmic_bytes() / per / 1e9, 4), unit="GB/s",
-                cores=threads, kind="oracle",
-                sample=f"the full step of {case.name}, {reps} repetitions, "
-                       f"{per * 1e3:.1f} ms each, fp64 C oracle with OpenMP over (b, h)",
-                ms_per_step=round(per * 1e3, 3))
+    per, reps = time_oracle(case, threads, budget_s)
+    one, reps1 = time_oracle(case, 1, budget_s)
+    gbs = lambda t: round(case.algorithmic_bytes() / t / 1e9, 4)
+    return dict(value=gbs(per), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"the full step of {case.name}: median of {reps} repetitions "
+                       f"({per * 1e3:.1f} ms each) on {threads} threads, and of {reps1} "
+                       f"({one * 1e3:.1f} ms each) on one; fp64 C oracle, OpenMP over (b, h)",
+                ms_per_step=round(per * 1e3, 3),
+                single_thread=dict(value=gbs(one), unit="GB/s", ms_per_step=round(one * 1e3, 3),
+                                   reps=reps1),
+                reps=reps, **cpu_description())
 
 
 # The flash-decoding-bench design note's sweep: decode steps (one query token)
@@ -301,9 +434,9 @@ SWEEP_SHAPE = dict(H=32, Hkv=32, d=128, bs=16, dtype="f16")
 def point(case, dev, steps, warmup, use_graph, parts):
     """One measured configuration: partition count, µs per step, live GB/s."""
     import torch
-    w, ts, err = measure(case, dev, steps, warmup, use_graph, parts)
+    w, ts, tmin, err = measure(case, dev, steps, warmup, use_graph, parts)
     row = dict(partitions=w.P, v_slices=w.v_slices, us=round(ts * 1e6, 3),
-               GBps=round(w.bytes / ts / 1e9, 1),
+               us_min=round(tmin * 1e6, 3), GBps=round(w.bytes / ts / 1e9, 1),
                max_abs_err=err, algorithmic_bytes=w.bytes)
     del w
     torch.cuda.empty_cache()
@@ -407,10 +540,11 @@ def sweep(dev, steps, warmup, use_graph):
                                      f"Hkv={sh['Hkv']} d={sh['d']} bs={sh['bs']}")
             row = dict(batch=batch, kv_len=kv, algorithmic_bytes=case.algorithmic_bytes())
             for label, parts in (("single", 1), ("split", 0)):
-                w, ts, err = measure(case, dev, steps, warmup, use_graph, parts)
+                w, ts, tmin, err = measure(case, dev, steps, warmup, use_graph, parts)
                 row[f"{label}_partitions"] = w.P
                 row[f"{label}_v_slices"] = w.v_slices
                 row[f"{label}_us"] = round(ts * 1e6, 3)
+                row[f"{label}_us_min"] = round(tmin * 1e6, 3)
                 row[f"{label}_GBps"] = round(w.bytes / ts / 1e9, 1)
                 row[f"{label}_max_abs_err"] = err
                 del w
@@ -435,6 +569,68 @@ def sweep(dev, steps, warmup, use_graph):
         crossover_kv_len=crossover, points=points)
 
 
+def leg_row(cid, parts, dev, steps, warmup, use_graph, reps):
+    """One per-config leg: workload cid at partition count parts (0 = the
+    heuristic), parity-gated and timed like the headline."""
+    import pa_inputs as pi
+    w, ts, tmin, err = measure(pi.make_config_case(cid), dev, steps, warmup, use_graph, parts,
+                               reps)
+    return dict(
+        workload=cid, name=w.case.name, status="ok", partitions=w.P, v_slices=w.v_slices,
+        path=("single-pass" if w.P == 1 else "split-KV + fused merge")
+             + (", V split in two" if w.v_slices > 1 else ""),
+        us_per_step=round(ts * 1e6, 3), us_min=round(tmin * 1e6, 3),
+        GBps=round(w.bytes / ts / 1e9, 1),
+        pct_of_peak=round(100 * w.bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
+        launches_per_step=w.launches_per_step(), max_abs_err=err,
+        rotation_copies=w.ncopies, algorithmic_bytes=w.bytes)
+
+
+# A child that ends on a signal or an abort has faulted or crashed: its
+# device state is gone, and nothing more is run on the GPU after it.
+CRASH_CODES = (134, 137, 139)
+
+
+def child_legs(args, plan, python=None):
+    """Each (workload, partitions) leg of `plan` in a fresh child process (a
+    subprocess, not an exec of this one).  Returns (rows, crashed): a leg
+    whose child faulted, crashed or hung is reported as CRASH and ends the
+    run, as a fault that poisons the device context would; one that failed
+    normally (e.g. its parity gate) is reported as FAILED."""
+    import subprocess
+    rows = []
+    for cid, parts in plan:
+        cmd = [python or sys.executable, "-u", os.path.abspath(__file__), "--leg", f"{cid}:{parts}",
+               "--steps", str(min(args.steps, 1000)), "--warmup", str(args.warmup),
+               "--reps", str(args.reps)]
+        if args.eager:
+            cmd.append("--eager")
+        if args.variant:
+            cmd += ["--variant", args.variant]
+        try:
+            res = subprocess.run(cmd, capture_output=True, text=True, timeout=600, cwd=ROOT)
+            rc, out, err = res.returncode, res.stdout, res.stderr
+        except subprocess.TimeoutExpired as e:
+            rc, out, err = -9, "", (e.stderr or b"").decode(errors="replace") \
+                if isinstance(e.stderr, bytes) else (e.stderr or "")
+        sys.stderr.write(err)
+        lines = [l for l in out.splitlines() if l.strip()]
+        if rc == 0 and lines:
+            row = json.loads(lines[-1])
+            log(f"workload {cid} P={row['partitions']}: {row['us_per_step']:.2f} us/step "
+                f"(min {row['us_min']:.2f}) {row['GBps']:.0f} GB/s")
+            rows.append(row)
+            continue
+        crashed = rc < 0 or rc in CRASH_CODES
+        status = "CRASH" if crashed else "FAILED"
+        log(f"workload {cid} partitions={parts}: {status} (child exit status {rc})")
+        rows.append(dict(workload=cid, requested_partitions=parts, status=status, rc=rc,
+                         stderr_tail=err[-400:]))
+        if crashed:
+            return rows, True
+    return rows, False
+
+
 def main():
     global VARIANT
     args = parse()
@@ -443,6 +639,36 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step has no multi-GPU path in this library)", file=sys.stderr)
         sys.exit(2)
+    if args.reps < 1:
+        sys.exit("--reps must be at least 1")
+    use_graph = not args.eager
+
+    if args.leg:                          # a child: one per-config leg, one JSON row
+        import torch
+        import paged_attention_decode_pa_amd as pa
+        if not torch.cuda.is_available():
+            sys.exit("bench.py needs a GPU")
+        pa.load()
+        if VARIANT:
+            pa.load_variant(VARIANT)
+        cid, parts = (int(x) for x in args.leg.split(":"))
+        print(json.dumps(leg_row(cid, parts, torch.device("cuda:0"), args.steps, args.warmup,
+                                 use_graph, args.reps)), flush=True)
+        return
+
+    # the per-config legs first, each in its own process, before this process
+    # touches the GPU
+    per_config = []
+    if not args.no_per_config and not args.case and not args.sweep:
+        plan = [(c, 0) for c in (1, 2, 3, 4, 5) if c != args.workload] + [(4, 1), (5, 1)]
+        per_config, crashed = child_legs(args, plan)
+        if crashed:
+            print(json.dumps({"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
+                              "steps": args.steps, "warmup": args.warmup,
+                              "status": "CRASH in a per-config leg; nothing more was run",
+                              "per_config": per_config}), flush=True)
+            sys.exit(3)
+
     import torch
     import pa_inputs as pi
     import paged_attention_decode_pa_amd as pa
@@ -452,7 +678,6 @@ def main():
     if VARIANT:
         pa.load_variant(VARIANT)
     dev = torch.device("cuda:0")
-    use_graph = not args.eager
     if args.sweep:
         fn = {"design-note": sweep, "ragged": sweep_ragged, "script": sweep_script,
               "shapes": sweep_shapes}[args.sweep]
@@ -466,34 +691,31 @@ def main():
                                 name=f"{dt} B={B} ctx={ctx} H={H} Hkv={Hkv} d={d} bs={bs}")
     else:
         headline = pi.make_config_case(args.workload)
-    per_config = []
-    if not args.no_per_config and not args.case:
-        plan = [(c, 0) for c in (1, 2, 3, 4, 5) if c != args.workload] + [(4, 1), (5, 1)]
-        for cid, parts in plan:
-            w, ts, err = measure(pi.make_config_case(cid), dev, min(args.steps, 1000),
-                                 args.warmup, use_graph, parts)
-            per_config.append(dict(
-                workload=cid, name=w.case.name, partitions=w.P, v_slices=w.v_slices,
-                path=("single-pass" if w.P == 1 else "split-KV + fused merge")
-                     + (", V split in two" if w.v_slices > 1 else ""),
-                us_per_step=round(ts * 1e6, 3), GBps=round(w.bytes / ts / 1e9, 1),
-                pct_of_peak=round(100 * w.bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
-                launches_per_step=1 if w.single_launch() else 2, max_abs_err=err,
-                rotation_copies=w.ncopies, algorithmic_bytes=w.bytes))
-            log(f"workload {cid} P={w.P}: {ts * 1e6:.2f} us/step "
-                f"{w.bytes / ts / 1e9:.0f} GB/s")
-            del w
-            torch.cuda.empty_cache()
 
-    w, t_step, err = measure(headline, dev, args.steps, args.warmup, use_graph, args.partitions)
+    w, t_step, t_min, err = measure(headline, dev, args.steps, args.warmup, use_graph,
+                                    args.partitions, args.reps)
     gbs = w.bytes / t_step / 1e9
-    log(f"timed workload {headline.name} P={w.P}: {t_step * 1e6:.2f} us/step {gbs:.0f} GB/s")
+    log(f"timed workload {headline.name} P={w.P}: {t_step * 1e6:.2f} us/step (median of "
+        f"{args.reps} regions of {args.steps} steps; min {t_min * 1e6:.2f}) {gbs:.0f} GB/s")
     if not w.single_launch():
         raise SystemExit("the headline step must be a single kernel launch")
-    # the step is one launch of the dominant kernel: its timed region is the step's
+    # the step is one launch of the dominant kernel: its timed regions are the step's
     t_dom, dom_bytes = t_step, w.bytes
     dom_gbs = dom_bytes / t_dom / 1e9
     c = w.case
+    grid = c.num_kv_heads * c.batch * w.P * w.v_slices
+    ncopies, P, v_slices, kname = w.ncopies, w.P, w.v_slices, w.kernel_name()
+    del w
+    torch.cuda.empty_cache()
+
+    read = None
+    if not args.no_read_ceiling:
+        r_med, r_min, r_bytes = read_ceiling(dev, dom_bytes, grid, args.steps, args.warmup,
+                                             use_graph, args.reps)
+        read = dict(us=r_med * 1e6, us_min=r_min * 1e6, bytes=r_bytes)
+        log(f"read ceiling: {r_bytes} bytes by {grid} workgroups in {r_med * 1e6:.2f} us "
+            f"(min {r_min * 1e6:.2f}), {r_bytes / r_med / 1e9:.0f} GB/s")
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.randn(n // 2, device=dev).to(torch.bfloat16)
@@ -507,6 +729,27 @@ def main():
     if args.cpu_seconds > 0:
         base = cpu_baseline(headline, args.cpu_seconds)
 
+    roofline = {
+        "bound": "hbm",
+        "kernel": kname,
+        "achieved": round(dom_gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None if VARIANT else recorded_traffic(c.name),
+        "avg_launch_us": round(t_dom * 1e6, 3),
+        "launches_per_step": 1,
+        "bytes_per_launch": dom_bytes,
+        "workgroups": grid,
+    }
+    if read is not None:
+        roofline.update({
+            "read_ceiling_us": round(read["us"], 3),
+            "read_ceiling_us_min": round(read["us_min"], 3),
+            "read_ceiling_GBps": round(read["bytes"] / read["us"] / 1e3, 1),
+            "read_ceiling_bytes": read["bytes"],
+            "frac_of_read_ceiling": round(read["us"] / (t_dom * 1e6), 4),
+        })
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -516,6 +759,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 6),
         "us_per_step": round(t_step * 1e6, 3),
+        "us_min": round(t_min * 1e6, 3),
+        "reps": args.reps,
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -523,29 +768,19 @@ def main():
         "dtype": c.dtype,
         "data": "synthetic",
         "config": {
-            "workload": c.name + (" split-KV (Flash-Decoding) + merge" if w.P > 1
+            "workload": c.name + (" split-KV (Flash-Decoding) + merge" if P > 1
                                   else " single-pass"),
             "batch": c.batch, "context_len": int(c.context_lens[0]),
             "num_heads": c.num_heads, "num_kv_heads": c.num_kv_heads,
             "head_dim": c.head_dim, "block_size": c.block_size,
-            "pool_blocks": c.num_pool_blocks, "num_partitions": w.P,
-            "v_slices": w.v_slices,
-            "algorithmic_bytes_per_step": w.bytes, "rotation_copies": w.ncopies,
-            "timing": "HIP graph replay of K steps" if use_graph else "eager launches",
+            "pool_blocks": c.num_pool_blocks, "num_partitions": P, "v_slices": v_slices,
+            "algorithmic_bytes_per_step": dom_bytes, "rotation_copies": ncopies,
+            "timing": (f"median of {args.reps} regions of {args.steps} steps, replayed back to "
+                       "back from HIP graphs" if use_graph else
+                       f"median of {args.reps} regions of {args.steps} eager steps"),
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": w.kernel_name(),
-            "achieved": round(dom_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if VARIANT else recorded_traffic(c.name),
-            "avg_launch_us": round(t_dom * 1e6, 3),
-            "launches_per_step": 1,
-            "bytes_per_launch": dom_bytes,
-        },
+        "roofline": roofline,
         "cpu_baseline": base,
         "library": (f"ablation build {VARIANT} ({os.path.basename(pa.VARIANT_PATHS[VARIANT])})"
                     if VARIANT else os.path.basename(pa.LIB_PATH)),

@@ -9,6 +9,10 @@ sources with PA_QK_VALU=1: the q.K product of the 16-bit, head-dim-128,
 4-heads-per-kv-head kernels on the vector ALUs instead of the matrix cores,
 all else identical.  It exists only to measure what the matrix cores bring
 (bench.py --variant valu_qk); the package never loads it by itself.
+
+libpa_read_probe.so (csrc/pa_read_probe.hip, include/pa_read_probe.h) is a
+plain streaming read with the decode kernel's load shape, the ceiling
+bench.py measures the decode kernel against; nothing else loads it.
 """
 import os
 import subprocess
@@ -22,6 +26,8 @@ SOURCES = [os.path.join(CSRC, f) for f in
            ("pa_decode.hip", "pa_kernels_f32.hip", "pa_kernels_bf16.hip", "pa_kernels_f16.hip")]
 KERNEL_SOURCES = SOURCES[1:]
 LIB = os.path.join(HERE, "libpa_decode.so")
+PROBE_SOURCES = [os.path.join(CSRC, "pa_read_probe.hip")]
+PROBE_LIB = os.path.join(HERE, "libpa_read_probe.so")
 # name -> (library file, extra compiler flags)
 VARIANTS = {
     "valu_qk": (os.path.join(HERE, "libpa_decode_valu_qk.so"), ["-DPA_QK_VALU=1"]),
@@ -64,19 +70,23 @@ def compile_objects(sources, outdir, extra=()):
 
 
 def build(verbose: bool = False, variants=tuple(VARIANTS)) -> str:
-    """Compile and link libpa_decode.so and the named ablation libraries (all
-    objects compile in parallel).  Returns the path of libpa_decode.so."""
-    jobs = [(LIB, [])] + [VARIANTS[v] for v in variants]
+    """Compile and link libpa_decode.so, the named ablation libraries and the
+    read probe (all objects compile in parallel).  Returns the path of
+    libpa_decode.so."""
+    jobs = [(LIB, [], SOURCES)] + [VARIANTS[v] + (SOURCES,) for v in variants]
+    jobs.append((PROBE_LIB, [], PROBE_SOURCES))
     with tempfile.TemporaryDirectory() as tmp:
         if verbose:
             print(f"{HIPCC} {' '.join(FLAGS)} -c <each of {len(SOURCES)} sources>"
                   + "".join(f", again with {' '.join(f)} for {os.path.basename(l)}"
-                            for l, f in jobs[1:]), flush=True)
+                            for l, f, _ in jobs[1:-1])
+                  + f"; {os.path.basename(PROBE_LIB)} from "
+                  + ", ".join(os.path.basename(x) for x in PROBE_SOURCES), flush=True)
         procs = []
-        for n, (lib, extra) in enumerate(jobs):
+        for n, (lib, extra, sources) in enumerate(jobs):
             outdir = os.path.join(tmp, str(n))
             os.mkdir(outdir)
-            procs.append((lib, compile_objects_async(SOURCES, outdir, extra)))
+            procs.append((lib, compile_objects_async(sources, outdir, extra)))
         for lib, pending in procs:
             objs = []
             for src, obj, p in pending:

@@ -40,3 +40,57 @@ def test_source_digest_ignores_comments_only():
     assert strip(code) == strip(same)
     assert strip(code) != strip(changed)
     assert strip(code) != strip(literal)
+
+
+def _args(**kw):
+    import argparse
+    d = dict(steps=20, warmup=1, reps=5, eager=False, variant=None)
+    d.update(kw)
+    return argparse.Namespace(**d)
+
+
+def test_child_leg_failure_is_reported_and_the_run_goes_on():
+    # without a GPU each child leg exits with an error of its own: every leg
+    # is still tried, and each is reported as FAILED (not a crash)
+    import torch
+    if torch.cuda.is_available():
+        import pytest
+        pytest.skip("a GPU is present")
+    rows, crashed = bench.child_legs(_args(), [(1, 0), (4, 1)])
+    assert not crashed
+    assert [r["workload"] for r in rows] == [1, 4]
+    assert all(r["status"] == "FAILED" and r["rc"] == 1 for r in rows)
+    assert "needs a GPU" in rows[0]["stderr_tail"]
+
+
+def test_child_leg_crash_ends_the_run(tmp_path):
+    # a child that ends on SIGABRT (as after a device fault) is a CRASH, and
+    # no later leg is started
+    fake = tmp_path / "aborting_python"
+    fake.write_text("#!/bin/sh\nkill -ABRT $$\n")
+    fake.chmod(0o755)
+    rows, crashed = bench.child_legs(_args(), [(2, 0), (3, 0), (5, 1)], python=str(fake))
+    assert crashed
+    assert len(rows) == 1
+    assert rows[0]["workload"] == 2 and rows[0]["status"] == "CRASH" and rows[0]["rc"] < 0
+
+
+def test_cpu_baseline_reports_one_thread_and_the_host():
+    import pa_inputs as pi
+    case = pi.make_config_case(1)
+    base = bench.cpu_baseline(case, 0.1)
+    one = base["single_thread"]
+    assert one["value"] > 0 and one["ms_per_step"] > 0 and one["reps"] >= 1
+    assert base["reps"] >= 1
+    assert base["logical_cpus"] >= 1 and base["usable_cpus"] >= 1
+    assert base["physical_cores"] is None or base["physical_cores"] >= 1
+    assert "one" in base["sample"]
+
+
+def test_rotation_and_summary():
+    # >= 1 GiB of distinct copies, capped; median of an even count averages
+    assert bench.rotation_copies(67129344) == 16
+    assert bench.rotation_copies(1 << 20) == bench.MAX_COPIES
+    assert bench.rotation_copies(1 << 31) == 2
+    assert bench.summarize([3.0, 1.0, 2.0]) == (2.0, 1.0)
+    assert bench.summarize([4.0, 1.0, 2.0, 3.0]) == (2.5, 1.0)

@@ -39,6 +39,11 @@ def test_bench_prints_one_consistent_json_line(gpu):
     assert r["bytes_per_launch"] == bytes_per_step
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+    assert c["single_thread"]["value"] > 0
+    # median and min of the timed regions; the read ceiling beside the kernel
+    assert d["reps"] == 5 and 0 < d["us_min"] <= d["us_per_step"]
+    assert r["read_ceiling_us"] > 0 and r["read_ceiling_bytes"] >= bytes_per_step
+    assert abs(r["frac_of_read_ceiling"] - r["read_ceiling_us"] / r["avg_launch_us"]) < 1e-3
 
 
 def test_bench_case_option_reports_its_launch(gpu):
