@@ -295,3 +295,23 @@ def test_decode_helper_refuses_mismatched_tensors_before_any_launch():
     assert code() == pa.PA_ERR_DEVICE
     assert code(out=torch.zeros(B, H, d, dtype=torch.bfloat16),
                 workspace=torch.zeros(64, dtype=torch.uint8)) == pa.PA_ERR_DEVICE
+
+
+def test_read_probe_library_exports_its_header():
+    # the measuring aid beside the library: what include/pa_read_probe.h declares
+    import ctypes
+    from paged_attention_decode_pa_amd import build as hip_build
+    text = open(os.path.join(os.path.dirname(HEADER), "pa_read_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+    assert names == ["pa_probe_read"]
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    fn = lib.pa_probe_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    # argument checks come before any HIP call
+    assert fn(None, 1024, 4, 16, 16, None) == -1
+    assert fn(16, -1, 4, 16, 16, None) == -2
+    assert fn(16, 1024, 0, 16, 16, None) == -2
+    assert fn(16, 1024, 4, 12, 16, None) == -3
+
