@@ -173,6 +173,29 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
                  size_t workspace_bytes);
 
 /*
+ * pa_decode without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, same launch (heuristic partition count)
+ * and same results as pa_decode; the fused split's tickets and partials live
+ * in a fixed device array of 64 MiB inside the library (one per device, held
+ * until the process ends) instead of library-owned allocations, so the call
+ * never allocates, frees or synchronises.  The first call on a device takes
+ * that device's array address and enqueues a small kernel on `stream` that
+ * clears the tickets; every call leaves them clear.  Limit: the array holds
+ * 65536 tickets (256 KiB) and 63.75 MiB of partials, so a split with
+ * B * Hkv > 65536 or pa_workspace_bytes(B, H, d, P) > 63.75 MiB returns
+ * PA_ERR_WORKSPACE before launching anything (the single pass needs none).
+ * All calls on one device share the array: calls that may overlap in time on
+ * one device (on different streams, or graph replays beside other calls) race
+ * on it and must be ordered by the caller.  Returns PA_OK or a negative
+ * PA_ERR_* code, as pa_decode.
+ */
+int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, int B, int H,
+                      int Hkv, int d, int block_size, int max_blocks, float scale, int dtype,
+                      void *stream);
+
+/*
  * The two halves of the split path, for callers that schedule them apart or
  * time them separately (Flash-Decoding's per-chunk pass and its merge).
  * pa_decode_partials runs only the split kernel: for every (b, h) and

@@ -35,7 +35,8 @@ PA_ERR_DEVICE = -8
 PA_ERR_ALIAS = -9
 PA_ERR_VALUE = -10
 
-EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_partials", "pa_merge_partials",
+EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_decode_partials",
+           "pa_merge_partials",
            "pa_workspace_bytes", "pa_choose_partitions", "pa_plan", "pa_device_num_cus",
            "pa_strerror", "pa_release")
 
@@ -63,6 +64,7 @@ def load(path: Optional[str] = None):
     core = [V, V, V, V, V, V, I, I, I, I, I, I, F, I, V]
     lib.pa_decode.argtypes = core
     lib.pa_decode_ex.argtypes = core + [I, LL, V, SZ]
+    lib.pa_decode_noalloc.argtypes = core
     lib.pa_decode_partials.argtypes = [V, V, V, V, V, I, I, I, I, I, I, F, I, I, LL, V, SZ, V]
     lib.pa_merge_partials.argtypes = [V, V, SZ, I, I, I, I, I, V]
     lib.pa_workspace_bytes.argtypes = [I, I, I, I]
@@ -75,7 +77,8 @@ def load(path: Optional[str] = None):
     lib.pa_strerror.restype = ctypes.c_char_p
     lib.pa_release.argtypes = []
     lib.pa_release.restype = None
-    for name in ("pa_decode", "pa_decode_ex", "pa_decode_partials", "pa_merge_partials",
+    for name in ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_decode_partials",
+                 "pa_merge_partials",
                  "pa_choose_partitions", "pa_plan", "pa_device_num_cus"):
         getattr(lib, name).restype = I
     if path is None:
@@ -143,6 +146,14 @@ def pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv
                              max_blocks, scale, dtype, _stream(stream), num_partitions,
                              num_pool_blocks, _ptr(workspace), workspace_bytes)
     _check(rc, "pa_decode_ex")
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
+                      block_size, max_blocks, scale, dtype, stream=None) -> None:
+    rc = load().pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), _ptr(context_lens), B, H, Hkv, d,
+                                  block_size, max_blocks, scale, dtype, _stream(stream))
+    _check(rc, "pa_decode_noalloc")
 
 
 def pa_decode_partials(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,

@@ -355,6 +355,51 @@ int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cu
     return clamp_partitions((int)tiles, (int)P);
 }
 
+// ---- the allocation-free entry point's scratch -----------------------------
+// pa_decode_noalloc keeps the fused split's tickets and partials in this
+// file-scope device array instead of library-owned allocations: each device
+// the library runs on holds one copy for the life of the process.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address is taken once per device with hipGetSymbolAddress and kept
+// in g_scratch_ptr, and only that address reaches kernels.  Layout: a fixed
+// region of kScratchTickets tickets from offset 0 (a call uses the first
+// B * Hkv), then the partials (the workspace layout of the split path) from
+// kScratchPartials on.  The ticket region is never used for anything else,
+// so the zeros the set-up writes and every call leaves behind hold whatever
+// shapes the calls have.
+constexpr size_t kScratchBytes = 64u << 20;
+constexpr size_t kScratchTickets = 1u << 16;
+constexpr size_t kScratchPartials = kScratchTickets * sizeof(int);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::map<int, char *> g_scratch_ptr;  // device -> address of its `scratch`
+
+__global__ void clear_words(unsigned *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The device address of this device's `scratch`, set up on first use: the
+// address is taken with the device current, and the ticket region is zeroed
+// by a fill kernel enqueued on `stream` (ordered before the call's kernels; a
+// kernel, not a memset, so that a capture may hold it).  The caller holds
+// g_mutex.
+int scratch_for(int dev, hipStream_t stream, char **out) {
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return PA_OK;
+    }
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+    const int n = (int)kScratchTickets;
+    hipLaunchKernelGGL(clear_words, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<unsigned *>(ptr), n);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char *>(ptr);
+    *out = static_cast<char *>(ptr);
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,7 +428,8 @@ const char *pa_strerror(int code) {
         case PA_ERR_ALIGN: return "pointer alignment (16 bytes for tensors, 4 for int32 arrays)";
         case PA_ERR_WORKSPACE:
             return "workspace missing or too small, or the library would allocate one while the "
-                   "stream is being captured";
+                   "stream is being captured, or pa_decode_noalloc needs more than its 64 MiB "
+                   "scratch";
         case PA_ERR_HIP: return "HIP runtime call or kernel launch failed";
         case PA_ERR_DEVICE: return "no usable HIP device";
         case PA_ERR_ALIAS: return "out overlaps an input";
@@ -454,6 +500,40 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
               int d, int block_size, int max_blocks, float scale, int dtype, void *stream) {
     return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                         block_size, max_blocks, scale, dtype, stream, 0, 0, nullptr, 0);
+}
+
+int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, int B, int H,
+                      int Hkv, int d, int block_size, int max_blocks, float scale, int dtype,
+                      void *stream) {
+    Validated v;
+    int rc = validate(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
+                      block_size, max_blocks, scale, dtype, true, &v);
+    if (rc != PA_OK) return rc;
+    if (B == 0) return PA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if ((rc = current_device(&dev)) != PA_OK) return rc;
+    const int cus = device_cus(dev);
+    if (cus < 0) return cus;
+    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, cus, 0, false);
+    const int P = plan.P;
+    Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
+                           max_blocks, block_size, scale, v.esize, 0, P);
+    p.part_tiles_log2 = plan.part_tiles_log2;
+    p.solo_tiles = plan.solo_tiles;
+    p.out = out;
+    if (P == 1) return run_main(p, dtype, d, v.G, plan.mode, s);
+    const size_t units = (size_t)B * Hkv;
+    if (units > kScratchTickets ||
+        workspace_layout(B, H, P, d).total > kScratchBytes - kScratchPartials)
+        return PA_ERR_WORKSPACE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    char *base = nullptr;
+    if ((rc = scratch_for(dev, s, &base)) != PA_OK) return rc;
+    p.counters = reinterpret_cast<int *>(base);
+    attach_workspace(p, base + kScratchPartials, d);
+    return run_main(p, dtype, d, v.G, plan.mode, s);
 }
 
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,

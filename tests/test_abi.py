@@ -315,3 +315,22 @@ def test_read_probe_library_exports_its_header():
     assert fn(16, 1024, 0, 16, 16, None) == -2
     assert fn(16, 1024, 4, 12, 16, None) == -3
 
+
+
+def test_noalloc_entry_validates_like_pa_decode():
+    # the allocation-free entry takes pa_decode's arguments and refuses the
+    # same invalid ones before any HIP call
+    lib = pa.load()
+    base = [FAKE["out"], FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 2, 32, 8, 128,
+            16, 4, 0.088, 1, None]
+    for change, code in ((dict(i=7, v=31), pa.PA_ERR_SHAPE), (dict(i=9, v=96),
+                                                              pa.PA_ERR_UNSUPPORTED),
+                         (dict(i=13, v=7), pa.PA_ERR_DTYPE), (dict(i=0, v=None), pa.PA_ERR_NULL),
+                         (dict(i=12, v=float("nan")), pa.PA_ERR_VALUE)):
+        args = list(base)
+        args[change["i"]] = change["v"]
+        assert lib.pa_decode_noalloc(*args) == code
+        assert lib.pa_decode(*args) == code
+    args = list(base)
+    args[6] = 0
+    assert lib.pa_decode_noalloc(*args) == pa.PA_OK   # B == 0: nothing to do
