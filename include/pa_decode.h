@@ -182,9 +182,10 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
  * never allocates, frees or synchronises.  The first call on a device takes
  * that device's array address and enqueues a small kernel on `stream` that
  * clears the tickets; every call leaves them clear.  Limit: the array holds
- * 65536 tickets (256 KiB) and 63.75 MiB of partials, so a split with
- * B * Hkv > 65536 or pa_workspace_bytes(B, H, d, P) > 63.75 MiB returns
- * PA_ERR_WORKSPACE before launching anything (the single pass needs none).
+ * 16384 tickets (2 MiB, one 128-byte line each) and 62 MiB of partials, so a
+ * split with B * Hkv > 16384 or pa_workspace_bytes(B, H, d, P) > 62 MiB
+ * returns PA_ERR_WORKSPACE before launching anything (the single pass needs
+ * none).
  * All calls on one device share the array: calls that may overlap in time on
  * one device (on different streams, or graph replays beside other calls) race
  * on it and must be ordered by the caller.  Returns PA_OK or a negative

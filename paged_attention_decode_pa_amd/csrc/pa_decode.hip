@@ -368,8 +368,8 @@ int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cu
 // so the zeros the set-up writes and every call leaves behind hold whatever
 // shapes the calls have.
 constexpr size_t kScratchBytes = 64u << 20;
-constexpr size_t kScratchTickets = 1u << 16;
-constexpr size_t kScratchPartials = kScratchTickets * sizeof(int);
+constexpr size_t kScratchTickets = 1u << 14;  // (sequence, kv head) units
+constexpr size_t kScratchPartials = kScratchTickets * kTicketStride * sizeof(int);
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 std::map<int, char *> g_scratch_ptr;  // device -> address of its `scratch`
 
@@ -391,7 +391,7 @@ int scratch_for(int dev, hipStream_t stream, char **out) {
     }
     void *ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
-    const int n = (int)kScratchTickets;
+    const int n = (int)(kScratchTickets * kTicketStride);
     hipLaunchKernelGGL(clear_words, dim3((n + 255) / 256), dim3(256), 0, stream,
                        static_cast<unsigned *>(ptr), n);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
@@ -475,7 +475,9 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     void *ws = nullptr;
     int *tickets = nullptr;
     std::lock_guard<std::mutex> lock(g_mutex);
-    if ((rc = library_buffers(dev, s, need, (size_t)B * Hkv, &ws, &tickets)) != PA_OK) return rc;
+    if ((rc = library_buffers(dev, s, need, (size_t)B * Hkv * kTicketStride, &ws, &tickets)) !=
+        PA_OK)
+        return rc;
     attach_workspace(p, ws, d);
     p.counters = tickets;
     return run_main(p, dtype, d, v.G, plan.mode, s);

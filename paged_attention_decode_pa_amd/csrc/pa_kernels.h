@@ -962,7 +962,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const int prev = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1,
+            const int prev = __hip_atomic_fetch_add(p.counters + (long long)kTicketStride * (b * p.Hkv + kvh), 1,
                                                     __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             const bool last = prev == VS * busy - 1;
             if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -972,7 +972,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         if (sm_last) {
             merge_group<DT, D, G, NW>(p, b, kvh, busy);
             if (threadIdx.x == 0)
-                __hip_atomic_store(p.counters + b * p.Hkv + kvh, 0, __ATOMIC_RELAXED,
+                __hip_atomic_store(p.counters + (long long)kTicketStride * (b * p.Hkv + kvh), 0, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     }
