@@ -70,10 +70,13 @@ def parse():
                          "length CTX, a scattered table over exactly the blocks needed, "
                          "DTYPE bf16|f16|f32); implies --no-per-config")
     ap.add_argument("--partitions", type=int, default=0,
-                    help="partition count for the timed workload (0 = the heuristic)")
-    ap.add_argument("--variant", default=None, choices=["valu_qk"],
+                    help="partition count for the timed workload (0 = the heuristic, "
+                         "-1 = the heuristic told that all lengths are equal)")
+    ap.add_argument("--variant", default=None, choices=["valu_qk", "no_vsplit", "ordered"],
                     help="time an ablation build instead of the library: valu_qk runs the "
-                         "q.K product on the vector ALUs instead of the matrix cores")
+                         "q.K product on the vector ALUs instead of the matrix cores; "
+                         "no_vsplit never splits V's head dim over two workgroups; ordered "
+                         "orders the fused merge by release / acquire")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (counter scale)")
     ap.add_argument("--reps", type=int, default=REPS,
@@ -83,11 +86,13 @@ def parse():
     ap.add_argument("--leg", default=None, metavar="WORKLOAD:PARTITIONS",
                     help=argparse.SUPPRESS)   # one per-config leg, run as a child process
     ap.add_argument("--sweep", nargs="?", const="design-note", default=None,
-                    choices=["design-note", "ragged", "script", "shapes"],
+                    choices=["design-note", "ragged", "script", "shapes", "uniform"],
                     help="instead of the headline, a sweep: design-note (single pass vs split "
                          "over batch 1/4 and KV 512..16384), ragged (long-tailed batches), "
                          "script (the benchmark script's default grid), shapes (the headline "
-                         "problem at other head dims, dtypes and block sizes)")
+                         "problem at other head dims, dtypes and block sizes), uniform "
+                         "(uniform batches covering the device: heuristic, uniform-lengths "
+                         "hint, single pass)")
     return ap.parse_args()
 
 
@@ -527,6 +532,30 @@ def sweep_shapes(dev, steps, warmup, use_graph):
                 data="synthetic", points=points)
 
 
+def sweep_uniform(dev, steps, warmup, use_graph):
+    """Uniform batches that cover the device (bf16, 32 query / 8 kv heads,
+    d 128, 16-token blocks): the heuristic (which splits sequences longer than
+    2048 tokens), the heuristic told that the lengths are equal
+    (PA_PARTITIONS_UNIFORM) and a forced single pass."""
+    import pa_inputs as pi
+    points = []
+    for B, ctx in ((32, 4096), (32, 8192), (64, 4096), (64, 8192), (128, 4096)):
+        case = pi.make_case(B, ctx, 32, 8, 128, 16, dtype="bf16", seed=B * 7 + ctx,
+                            name=f"bf16 B={B} ctx={ctx} H=32 Hkv=8 d=128 bs=16")
+        row = dict(batch=B, context_len=ctx)
+        for tag, parts in (("heuristic", 0), ("uniform_hint", -1), ("single", 1)):
+            r = point(case, dev, steps, warmup, use_graph, parts)
+            row.update({f"{tag}_{k}": v for k, v in r.items() if k != "algorithmic_bytes"})
+            row["algorithmic_bytes"] = r["algorithmic_bytes"]
+        log(f"uniform B={B} x {ctx}: heuristic P={row['heuristic_partitions']} "
+            f"{row['heuristic_us']:.1f} us, hint {row['uniform_hint_us']:.1f} us, single "
+            f"{row['single_us']:.1f} us")
+        points.append(row)
+    return dict(metric="decode step us, uniform batches covering the device", unit="us",
+                higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup, dtype="bf16",
+                data="synthetic", points=points)
+
+
 def sweep(dev, steps, warmup, use_graph):
     import torch
     import pa_inputs as pi
@@ -680,7 +709,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.sweep:
         fn = {"design-note": sweep, "ragged": sweep_ragged, "script": sweep_script,
-              "shapes": sweep_shapes}[args.sweep]
+              "shapes": sweep_shapes, "uniform": sweep_uniform}[args.sweep]
         print(json.dumps(fn(dev, min(args.steps, 500), args.warmup, use_graph)), flush=True)
         return
 

@@ -149,12 +149,23 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
               const int32_t *block_tables, const int32_t *context_lens, int B, int H, int Hkv,
               int d, int block_size, int max_blocks, float scale, int dtype, void *stream);
 
+/* num_partitions value of pa_decode_ex and pa_plan: the heuristic, told that
+ * every sequence of the batch has the same context length. */
+#define PA_PARTITIONS_UNIFORM (-1)
+
 /*
  * pa_decode with the choices exposed.
  *   num_partitions   0 = heuristic (as pa_decode), 1 = single pass, n > 1 =
  *                    P = min(n, W, 4096) partitions, W = max_blocks *
  *                    block_size / 16 the tiles of a table row, split as
- *                    above.
+ *                    above.  PA_PARTITIONS_UNIFORM = the heuristic for a
+ *                    batch whose context_lens are all equal (the caller's
+ *                    promise; the lengths are in device memory): when the
+ *                    B * Hkv units already fill the device it runs the single
+ *                    pass instead of splitting the sequences longer than 2048
+ *                    tokens, which only pays off when a few long sequences
+ *                    would otherwise set the pace; below that it is the
+ *                    heuristic.  Results are correct whatever the lengths.
  *   num_pool_blocks  0 = unknown; > 0 = table entries >= num_pool_blocks are
  *                    treated like -1 instead of being read (a guard against
  *                    out-of-range ids).
@@ -250,10 +261,11 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
  * length-based choice of the split (flash-decoding-bench design note,
  * implementations section) as pa_decode applies it: *partitions =
  * the context partition count P it uses (num_partitions as in pa_decode_ex:
- * 0 = heuristic, n > 0 = forced), *v_slices = 2 when each unit (P == 1) or
+ * 0 = heuristic, PA_PARTITIONS_UNIFORM, n > 0 = forced), *v_slices = 2 when
+ * each unit (P == 1) or
  * each partition (P > 1) is served by two workgroups, one per half of V's
  * head dim, else 1.  Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (B < 0, Hkv,
- * max_blocks or num_cus <= 0), PA_ERR_VALUE (num_partitions < 0) or
+ * max_blocks or num_cus <= 0), PA_ERR_VALUE (num_partitions < -1) or
  * PA_ERR_UNSUPPORTED (d or block_size not supported).
  */
 int pa_plan(int B, int Hkv, int d, int max_blocks, int block_size, int num_cus,

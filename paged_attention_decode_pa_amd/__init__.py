@@ -17,7 +17,9 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 # Ablation builds of the same sources (see build.py), loaded only on request.
-VARIANT_PATHS = {"valu_qk": os.path.join(HERE, "libpa_decode_valu_qk.so")}
+VARIANT_PATHS = {"valu_qk": os.path.join(HERE, "libpa_decode_valu_qk.so"),
+                 "no_vsplit": os.path.join(HERE, "libpa_decode_no_vsplit.so"),
+                 "ordered": os.path.join(HERE, "libpa_decode_ordered.so")}
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
@@ -34,6 +36,8 @@ PA_ERR_HIP = -7
 PA_ERR_DEVICE = -8
 PA_ERR_ALIAS = -9
 PA_ERR_VALUE = -10
+
+PA_PARTITIONS_UNIFORM = -1   # num_partitions: heuristic for equal context lengths
 
 EXPORTS = ("pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_decode_partials",
            "pa_merge_partials",

@@ -4,11 +4,16 @@ The kernels of each element type are a translation unit of their own
 (csrc/pa_kernels_<dtype>.hip) and compile in parallel with the host launcher
 (csrc/pa_decode.hip); the objects are then linked into libpa_decode.so.
 
-An ablation library, libpa_decode_valu_qk.so, is built beside it from the same
-sources with PA_QK_VALU=1: the q.K product of the 16-bit, head-dim-128,
-4-heads-per-kv-head kernels on the vector ALUs instead of the matrix cores,
-all else identical.  It exists only to measure what the matrix cores bring
-(bench.py --variant valu_qk); the package never loads it by itself.
+Ablation libraries are built beside it, each only to measure what one
+design choice brings; the package never loads them by itself:
+libpa_decode_valu_qk.so (PA_QK_VALU=1: the q.K product of the 16-bit,
+head-dim-128, 4-heads-per-kv-head kernels on the vector ALUs instead of the
+matrix cores; bench.py --variant valu_qk) and libpa_decode_no_vsplit.so
+(PA_SPLIT_V=0 in the launcher: never split V's head dim over two workgroups;
+bench.py --variant no_vsplit).  A third, libpa_decode_ordered.so
+(PA_ORDERED_TICKET=1), orders the fused merge's exchange of partial sums by
+release / acquire in the memory model instead of by cache policy (bench.py
+--variant ordered); it computes the same bits.  All else is identical.
 
 libpa_read_probe.so (csrc/pa_read_probe.hip, include/pa_read_probe.h) is a
 plain streaming read with the decode kernel's load shape, the ceiling
@@ -28,9 +33,14 @@ KERNEL_SOURCES = SOURCES[1:]
 LIB = os.path.join(HERE, "libpa_decode.so")
 PROBE_SOURCES = [os.path.join(CSRC, "pa_read_probe.hip")]
 PROBE_LIB = os.path.join(HERE, "libpa_read_probe.so")
-# name -> (library file, extra compiler flags)
+# name -> (library file, extra compiler flags, sources compiled with them; the
+# other sources' objects are the main library's)
 VARIANTS = {
-    "valu_qk": (os.path.join(HERE, "libpa_decode_valu_qk.so"), ["-DPA_QK_VALU=1"]),
+    "valu_qk": (os.path.join(HERE, "libpa_decode_valu_qk.so"), ["-DPA_QK_VALU=1"], SOURCES),
+    "no_vsplit": (os.path.join(HERE, "libpa_decode_no_vsplit.so"), ["-DPA_SPLIT_V=0"],
+                  SOURCES[:1]),
+    "ordered": (os.path.join(HERE, "libpa_decode_ordered.so"), ["-DPA_ORDERED_TICKET=1"],
+                KERNEL_SOURCES),
 }
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -73,7 +83,7 @@ def build(verbose: bool = False, variants=tuple(VARIANTS)) -> str:
     """Compile and link libpa_decode.so, the named ablation libraries and the
     read probe (all objects compile in parallel).  Returns the path of
     libpa_decode.so."""
-    jobs = [(LIB, [], SOURCES)] + [VARIANTS[v] + (SOURCES,) for v in variants]
+    jobs = [(LIB, [], SOURCES)] + [VARIANTS[v] for v in variants]
     jobs.append((PROBE_LIB, [], PROBE_SOURCES))
     with tempfile.TemporaryDirectory() as tmp:
         if verbose:
@@ -87,8 +97,9 @@ def build(verbose: bool = False, variants=tuple(VARIANTS)) -> str:
             outdir = os.path.join(tmp, str(n))
             os.mkdir(outdir)
             procs.append((lib, compile_objects_async(sources, outdir, extra)))
+        main_objs = {}
         for lib, pending in procs:
-            objs = []
+            objs = {}
             for src, obj, p in pending:
                 _, err = p.communicate()
                 if p.returncode != 0:
@@ -96,7 +107,14 @@ def build(verbose: bool = False, variants=tuple(VARIANTS)) -> str:
                                        f"({p.returncode}):\n{_clean(err)}")
                 if verbose and _clean(err).strip():
                     print(_clean(err), file=sys.stderr)
-                objs.append(obj)
+                objs[src] = obj
+            if lib == LIB:
+                main_objs = dict(objs)
+            elif lib != PROBE_LIB:
+                # a variant that recompiles only some sources links the rest
+                # from the main library's objects
+                objs = {src: objs.get(src, main_objs[src]) for src in SOURCES}
+            objs = list(objs.values())
             cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
             res = subprocess.run(cmd, capture_output=True, text=True)
             if res.returncode != 0:

@@ -39,6 +39,15 @@ constexpr int kMaxPartitions = 4096;
 // split in two runs as a single pass with V split instead (when allowed).
 constexpr int kShortTableTiles = 32;
 
+#ifndef PA_SPLIT_V
+#define PA_SPLIT_V 1
+#endif
+// Whether the launcher may split V's head dim over two workgroups (the
+// kSingleSplitV and kFusedSplitV modes).  The library is built with 1; the
+// ablation library libpa_decode_no_vsplit.so is built with 0 to measure what
+// the split costs and saves, all else identical.
+bool use_split_v(int d) { return PA_SPLIT_V != 0 && split_v_built(d); }
+
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 
 // Workspace layout: [B][H][P] float2 (max, sum) | [B][H][P][d] float partial
@@ -295,15 +304,22 @@ Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
     Plan plan{1, kSingle, 0, 0};  // forced counts: every partition up to min(n, P) busy
     const long long units = (long long)B * Hkv;
     const bool covered = units >= cus;
+    const bool uniform = num_partitions == PA_PARTITIONS_UNIFORM;
+    if (uniform) num_partitions = 0;
     if (num_partitions == 0) {
         plan.P = choose_partitions(B, Hkv, max_blocks, block_size, cus);
         // Two partitions of a short table lose to the single pass with V's
         // head dim split over the same two workgroups per unit, which needs
         // no merge (measured at 96-128 units: at 512 tokens the single pass is
         // 7-8 % faster, at 1024 tokens 4-9 % slower).
-        if (plan.P == 2 && split_v_built(d) &&
+        if (plan.P == 2 && use_split_v(d) &&
             table_tiles(max_blocks, block_size) <= kShortTableTiles && 2 * units <= cus)
             plan.P = 1;
+        // Told that every sequence has the same length, a batch whose units
+        // already cover the device runs as a single pass: with no long tail
+        // to cut, the split's partials and merges only cost (measured 6-10 %
+        // on uniform batches of 32-128 x 4096-8192 tokens).
+        if (uniform && covered) plan.P = 1;
         // a sequence uses the partitions its length fills: at least 8 tiles
         // each (none of 16 tiles or fewer splits), or, when the units alone
         // cover the device, 64 tiles each (none of 128 tiles or fewer splits)
@@ -317,12 +333,12 @@ Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
     if (plan.P == 1) {
         // A single pass whose units fill at most half of the compute units
         // runs as two workgroups per unit, each with half of V's head dim.
-        plan.mode = split_v_built(d) && 2 * units <= cus ? kSingleSplitV : kSingle;
+        plan.mode = use_split_v(d) && 2 * units <= cus ? kSingleSplitV : kSingle;
     } else if (caller_workspace) {
         plan.mode = kPartials;
     } else if (num_partitions == 0 && covered) {
         plan.mode = kFusedLate;  // most partitions of such a launch are empty
-    } else if (split_v_built(d) && 4 * units * plan.P <= cus) {
+    } else if (use_split_v(d) && 4 * units * plan.P <= cus) {
         // a split whose workgroups fill at most a quarter of the compute
         // units also splits V's head dim over two workgroups per partition
         // (measured: 32 -> 64 workgroups gains ~5 %; 128 -> 256 loses 10-18 %,
@@ -447,7 +463,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     int rc = validate(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                       block_size, max_blocks, scale, dtype, true, &v);
     if (rc != PA_OK) return rc;
-    if (num_partitions < 0 || num_pool_blocks < 0) return PA_ERR_VALUE;
+    if (num_partitions < PA_PARTITIONS_UNIFORM || num_pool_blocks < 0) return PA_ERR_VALUE;
     if (workspace && !aligned(workspace, 16)) return PA_ERR_ALIGN;
     if (B == 0) return PA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -487,7 +503,7 @@ int pa_plan(int B, int Hkv, int d, int max_blocks, int block_size, int num_cus,
             int num_partitions, int *partitions, int *v_slices_out) {
     if (!partitions || !v_slices_out) return PA_ERR_NULL;
     if (B < 0 || Hkv <= 0 || max_blocks <= 0 || num_cus <= 0) return PA_ERR_SHAPE;
-    if (num_partitions < 0) return PA_ERR_VALUE;
+    if (num_partitions < PA_PARTITIONS_UNIFORM) return PA_ERR_VALUE;
     if (!supported_head_dim(d) || block_size < kTile || block_size > kMaxBlockSize ||
         (block_size & (block_size - 1)) != 0)
         return PA_ERR_UNSUPPORTED;

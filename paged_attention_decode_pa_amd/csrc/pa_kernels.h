@@ -56,8 +56,10 @@
 // chosen over: PA_WAVES_PER_GROUP (4), PA_PIPELINE_DEPTH (2 tiles in flight
 // per wave), PA_K_ROWS (1 = the row K layout where k_rows_layout picks it,
 // 0 = the column layout everywhere), PA_KV_CACHE_POLICY (2 = non-temporal
-// K/V loads) and PA_QK_VALU (0; 1 = the vector-ALU q.K of the ablation
-// library libpa_decode_valu_qk.so, which is built and tested).
+// K/V loads), PA_QK_VALU (0; 1 = the vector-ALU q.K of the ablation
+// library libpa_decode_valu_qk.so, which is built and tested) and
+// PA_ORDERED_TICKET (0; 1 = the fused merge ordered by release / acquire, the
+// ablation library libpa_decode_ordered.so, also built and tested).
 #ifndef PA_KERNELS_H
 #define PA_KERNELS_H
 
@@ -563,6 +565,14 @@ __device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float
     return merge_chunked<32>(ml, acc, P, d);
 }
 
+#ifndef PA_ORDERED_TICKET
+#define PA_ORDERED_TICKET 0
+#endif
+// Whether the fused merge's ticket carries release / acquire ordering (see
+// the kernel's epilogue): 0 in the library, 1 in the ablation library
+// libpa_decode_ordered.so.
+constexpr bool kOrderedTicket = PA_ORDERED_TICKET != 0;
+
 // Cache-policy bits (sc1) that make a buffer access agent-coherent: loads
 // read past this XCD's L2, which may hold stale copies of lines other XCDs
 // have rewritten since.
@@ -945,27 +955,44 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         if (direct || silent) return;
         // Publish this partition and take a ticket; the last of the VS * `busy`
         // workgroups of (b, kvh) merges their partitions and resets the ticket
-        // for the next call.  Ordering, in the memory model's terms: every
-        // thread's partial stores are sequenced before the barrier, which
-        // synchronises the workgroup (workgroup scope) with thread 0; thread
-        // 0's ticket is an agent-scope release read-modify-write, so the
-        // stores of all threads happen before it.  The tickets of one (b, kvh)
-        // form a release sequence, so in the workgroup whose ticket reads
-        // VS * busy - 1 the agent-scope acquire fence that follows makes every
-        // earlier ticket -- and so every other workgroup's stores -- happen
-        // before it, and through the second barrier before every thread's
-        // merge loads.  Only the merging workgroup pays for the acquire (an
-        // invalidate of its caches).  (The waitcnt lets each wave's stores
-        // complete before the barrier, so the release has little left to wait
-        // for.)
+        // for the next call.
+        //
+        // Ordering (PA_ORDERED_TICKET = 0, the library): the partial sums are
+        // agent-scope atomic stores, which on this part write through to the
+        // device-coherent level (past every XCD's L2); the waitcnt returns only
+        // once each of this wave's stores is acknowledged there, and the
+        // barrier holds thread 0 until all four waves have passed theirs.  The
+        // ticket is an agent-scope atomic, performed at that same level and
+        // issued after the barrier, so when any workgroup's ticket reads
+        // VS * busy - 1 the stores behind every earlier ticket are already
+        // there.  The merger issues its loads after its ticket has returned,
+        // with the coherent cache policy (kCoherent), which reads past a stale
+        // L2 copy.  This rests on the cache policy of the stores and loads and
+        // on where atomics are performed, not on the HIP memory model: in the
+        // model the relaxed ticket orders nothing.
+        //
+        // PA_ORDERED_TICKET = 1 (the ablation library libpa_decode_ordered.so)
+        // orders the same exchange within the memory model: thread 0's ticket
+        // is an agent-scope release read-modify-write, so every thread's
+        // stores, sequenced before the barrier that synchronises the
+        // workgroup with thread 0, happen before it; the tickets of one
+        // (b, kvh) form a release sequence, so in the workgroup whose ticket
+        // reads VS * busy - 1 the agent-scope acquire fence that follows makes
+        // every other workgroup's stores happen before it, and through the
+        // second barrier before every thread's merge loads.  On gfx950 the
+        // release is an L2 writeback in every publishing workgroup, which
+        // queues: measured +1.2 us on one 16384-token sequence (256
+        // workgroups) and +47 % on a batch of 32 x 8192 tokens (2048).
         __shared__ int sm_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const int prev = __hip_atomic_fetch_add(p.counters + (long long)kTicketStride * (b * p.Hkv + kvh), 1,
-                                                    __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            int *ticket = p.counters + (long long)kTicketStride * (b * p.Hkv + kvh);
+            const int prev = __hip_atomic_fetch_add(
+                ticket, 1, kOrderedTicket ? __ATOMIC_RELEASE : __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
             const bool last = prev == VS * busy - 1;
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (kOrderedTicket && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             sm_last = last;
         }
         __syncthreads();

@@ -29,8 +29,9 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pa.EXPORTS)
 
 
-def test_ablation_library_exports_the_same_functions():
-    lib = pa.load_variant("valu_qk")
+@pytest.mark.parametrize("variant", ["valu_qk", "no_vsplit", "ordered"])
+def test_ablation_library_exports_the_same_functions(variant):
+    lib = pa.load_variant(variant)
     for name in declared_functions():
         assert hasattr(lib, name), name
 
@@ -119,7 +120,7 @@ def test_plan_rejects_bad_arguments():
     P, vs = ctypes.c_int(), ctypes.c_int()
     assert lib.pa_plan(1, 8, 128, 4, 16, 256, 0, None, ctypes.byref(vs)) == pa.PA_ERR_NULL
     bad = [((1, 0, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 0, 0), pa.PA_ERR_SHAPE),
-           ((-1, 8, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 256, -1), pa.PA_ERR_VALUE),
+           ((-1, 8, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 256, -2), pa.PA_ERR_VALUE),
            ((1, 8, 96, 4, 16, 256, 0), pa.PA_ERR_UNSUPPORTED), ((1, 8, 128, 4, 8, 256, 0), pa.PA_ERR_UNSUPPORTED)]
     for a, code in bad:
         assert lib.pa_plan(*a, ctypes.byref(P), ctypes.byref(vs)) == code, a
@@ -201,8 +202,15 @@ def test_ex_and_split_half_validation():
     lib = pa.load()
     args = [FAKE["out"], FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128,
             16, 64, 0.088, 1, None]
-    assert lib.pa_decode_ex(*args, -1, 0, None, 0) == pa.PA_ERR_VALUE
+    assert lib.pa_decode_ex(*args, -2, 0, None, 0) == pa.PA_ERR_VALUE
     assert lib.pa_decode_ex(*args, 0, -5, None, 0) == pa.PA_ERR_VALUE
+    # PA_PARTITIONS_UNIFORM passes validation (and then finds no device here)
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.pa_decode_ex(*args, pa.PA_PARTITIONS_UNIFORM, 0, None, 0) == pa.PA_ERR_DEVICE
+    assert lib.pa_decode_partials(FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32,
+                                  8, 128, 16, 64, 0.088, 1, -1, 0, 0x700000, 1 << 20,
+                                  None) == pa.PA_ERR_VALUE
     assert lib.pa_decode_ex(*args, 4, 0, 0x700004, 1 << 20) == pa.PA_ERR_ALIGN
     part = [FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128, 16, 64, 0.088,
             1]
@@ -334,3 +342,34 @@ def test_noalloc_entry_validates_like_pa_decode():
     args = list(base)
     args[6] = 0
     assert lib.pa_decode_noalloc(*args) == pa.PA_OK   # B == 0: nothing to do
+
+
+def test_plan_uniform_lengths_hint():
+    # PA_PARTITIONS_UNIFORM: a covering batch runs the single pass; below the
+    # CU count the hint changes nothing
+    cus = 256
+    assert pa.pa_plan(64, 8, 128, 512, 16, cus, 0) == (8, 1)
+    assert pa.pa_plan(64, 8, 128, 512, 16, cus, pa.PA_PARTITIONS_UNIFORM) == (1, 1)
+    for B, W in ((1, 1024), (4, 128), (16, 16), (2, 60)):
+        assert pa.pa_plan(B, 8, 128, W, 16, cus, pa.PA_PARTITIONS_UNIFORM) == \
+            pa.pa_plan(B, 8, 128, W, 16, cus, 0)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(64, 8, 128, 512, 16, cus, -2)
+    assert e.value.code == pa.PA_ERR_VALUE
+    lib = pa.load()
+    args = [FAKE["out"], FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128,
+            16, 8, 0.088, 1, None]
+    assert lib.pa_decode_ex(*args, -2, 0, None, 0) == pa.PA_ERR_VALUE
+
+
+def test_no_vsplit_ablation_plans_no_v_split():
+    # the ablation build differs only in never splitting V's head dim
+    import ctypes
+    lib = pa.load_variant("no_vsplit")
+    P, vs = ctypes.c_int(0), ctypes.c_int(0)
+    for B, W in ((1, 32), (16, 16), (1, 1024), (4, 128)):
+        assert lib.pa_plan(B, 8, 128, W, 16, 256, 0, ctypes.byref(P), ctypes.byref(vs)) == 0
+        assert vs.value == 1
+        ref = pa.pa_plan(B, 8, 128, W, 16, 256, 0)
+        if ref[1] == 1:
+            assert P.value == ref[0]

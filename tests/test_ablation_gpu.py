@@ -1,9 +1,18 @@
-"""Parity of the ablation build libpa_decode_valu_qk.so (q.K on the vector ALUs
-for 16-bit elements, head dim 128, 4 query heads per kv head) with the fp64
-oracle, through its C ABI, in every kernel mode that build changes: single
-pass, fused split, fused split with the late query (a batch covering the
-device), and the split kernel with the separate merge kernel.  Its timings
-only mean something if it computes the same decode step."""
+"""Parity of the ablation builds with the fp64 oracle, through their C ABI.
+
+libpa_decode_valu_qk.so (q.K on the vector ALUs for 16-bit elements, head dim
+128, 4 query heads per kv head): every kernel mode that build changes --
+single pass, fused split, fused split with the late query (a batch covering
+the device), and the split kernel with the separate merge kernel.
+
+libpa_decode_ordered.so (the fused merge ordered by release / acquire):
+every fused mode, and bit for bit the library's output, since it does the
+same arithmetic in the same order.
+
+libpa_decode_no_vsplit.so (never splits V's head dim): the launches whose V
+split it removes.
+
+Their timings only mean something if they compute the same decode step."""
 import ctypes
 import math
 
@@ -20,9 +29,9 @@ from gpu_util import DeviceCase, assert_close, check_host_preconditions, say, to
 pytestmark = pytest.mark.gpu
 
 
-def run_variant(case, dev, parts, workspace=False):
+def run_variant(case, dev, parts, workspace=False, variant="valu_qk"):
     check_host_preconditions(case)
-    lib = pa.load_variant("valu_qk")
+    lib = pa.load() if variant is None else pa.load_variant(variant)
     d = DeviceCase(case, dev)
     out = torch.empty_like(d.q)
     c = case
@@ -70,3 +79,33 @@ def test_valu_qk_covering_batch(gpu, dtype):
     say(f"valu_qk covering batch {dtype}")
     out = run_variant(case, gpu, 0)
     assert_close(to_f64(out), oracle.decode_case(case), dtype, f"valu_qk covering {dtype}")
+
+
+ORDERED_CASES = [
+    # (B, lens, H, Hkv, d, dtype, forced partitions (0 = heuristic))
+    (1, [16384], 32, 8, 128, "bf16", 0),     # fused split, 32 partitions
+    (4, [2048] * 4, 32, 8, 128, "bf16", 0),  # fused split, 8 partitions
+    (1, [512], 32, 8, 128, "bf16", 0),       # fused split with V split
+    (5, [0, 1, 17, 300, 1000], 32, 8, 128, "f32", 7),
+    (3, [700, 90, 2500], 16, 16, 64, "f16", 0),
+    (40, [2200, 300] * 20, 32, 8, 128, "bf16", 0),   # late-query fused split
+]
+
+
+@pytest.mark.parametrize("shape", ORDERED_CASES, ids=lambda s: f"B{s[0]}_{s[5]}_P{s[6]}")
+def test_ordered_ticket_build(gpu, shape):
+    B, lens, H, Hkv, d, dtype, parts = shape
+    case = pi.make_case(B, lens, H, Hkv, d, 16, dtype=dtype, seed=sum(lens) % 1000 + 5)
+    say(f"ordered ticket B={B} {dtype} P={parts}")
+    out = run_variant(case, gpu, parts, variant="ordered")
+    assert_close(to_f64(out), oracle.decode_case(case), dtype, f"ordered B={B}")
+    ref = run_variant(case, gpu, parts, variant=None)
+    assert torch.equal(out, ref), "the ordered build must compute the library's bits"
+
+
+@pytest.mark.parametrize("B,lens", [(1, [512]), (16, [256] * 16), (2, [60, 60])])
+def test_no_vsplit_build(gpu, B, lens):
+    case = pi.make_case(B, lens, 32, 8, 128, 16, dtype="bf16", seed=B + 31)
+    say(f"no_vsplit B={B}")
+    out = run_variant(case, gpu, 0, variant="no_vsplit")
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"no_vsplit B={B}")

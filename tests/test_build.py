@@ -31,7 +31,7 @@ def test_no_kernel_uses_scratch():
 
 def test_valu_qk_ablation_uses_no_scratch():
     """The ablation build's changed kernels (16-bit) also keep to registers."""
-    _, flags = hip_build.VARIANTS["valu_qk"]
+    _, flags, _ = hip_build.VARIANTS["valu_qk"]
     srcs = [s for s in hip_build.KERNEL_SOURCES if "f32" not in s]
     with tempfile.TemporaryDirectory() as tmp:
         results = hip_build.compile_objects(

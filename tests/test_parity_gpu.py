@@ -1068,3 +1068,19 @@ def test_context_lens_are_clamped(gpu, parts):
     ref_case.context_lens = np.array([64, 0, 30], dtype=np.int32)
     assert_close(to_f64(out), oracle.decode_case(ref_case), "bf16", f"clamp P={parts}")
     assert (out[1].float() == 0).all()
+
+
+@pytest.mark.parametrize("lens", [[2200] * 40, [2200, 300] * 20],
+                         ids=["uniform", "not-uniform"])
+def test_uniform_lengths_hint(gpu, lens):
+    # PA_PARTITIONS_UNIFORM on a batch covering the device runs the single
+    # pass; the result is right whether or not the lengths really are equal
+    case = pi.make_case(len(lens), lens, 32, 8, 128, 16, dtype="bf16", seed=len(set(lens)) + 90)
+    cus = pa.pa_device_num_cus(0)
+    assert pa.pa_plan(case.batch, 8, 128, case.max_blocks, 16, cus,
+                      pa.PA_PARTITIONS_UNIFORM) == (1, 1)
+    say(f"uniform-lengths hint, lengths {sorted(set(lens))}")
+    out = run_gpu(case, gpu, num_partitions=pa.PA_PARTITIONS_UNIFORM)
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", "uniform hint")
+    single = run_gpu(case, gpu, num_partitions=1)
+    assert torch.equal(out, single)
