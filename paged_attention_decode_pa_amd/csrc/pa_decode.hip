@@ -269,6 +269,7 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.tiles_log2 = log2_int(block_size / kTile);
     p.part_tiles_log2 = 0;  // every partition up to min(n, P) busy
     p.solo_tiles = 0;
+    p.merge_ways = 1;
     p.max_tiles = table_tiles(max_blocks, block_size);
     p.qk_scale = scale * kLog2e;
     return p;
@@ -348,6 +349,23 @@ Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
         plan.mode = kFused;
     }
     return plan;
+}
+
+// Workgroups that share each fused merge: kMergeWays when a unit's partials
+// are at least kSharedMergeBytes and every workgroup of the launch can be
+// resident at once (at most one per compute unit), since the waiting mergers
+// then wait only for running workgroups; else the last arrival merges alone.
+// A waiting merger learns that the last partition is in about a microsecond
+// after the last arrival does, so sharing pays only when reading the whole
+// unit's partials through one CU takes longer than that (measured, 4 ways:
+// -0.3 us with 64 KiB per unit, +0.4 to +0.7 us with 16 KiB or less).
+constexpr long long kSharedMergeBytes = 48 << 10;
+int merge_ways(int mode, int B, int Hkv, int G, int d, int P, int cus) {
+    if (mode != kFused && mode != kFusedSplitV) return 1;
+    if ((long long)P * G * d * 4 < kSharedMergeBytes) return 1;
+    const long long per_launch =
+        (long long)(B < kMaxGridY ? B : kMaxGridY) * Hkv * P * v_slices(mode);
+    return per_launch <= cus ? kMergeWays : 1;
 }
 
 int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {
@@ -496,6 +514,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         return rc;
     attach_workspace(p, ws, d);
     p.counters = tickets;
+    p.merge_ways = merge_ways(plan.mode, B, Hkv, v.G, d, P, cus);
     return run_main(p, dtype, d, v.G, plan.mode, s);
 }
 
@@ -551,6 +570,7 @@ int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void 
     if ((rc = scratch_for(dev, s, &base)) != PA_OK) return rc;
     p.counters = reinterpret_cast<int *>(base);
     attach_workspace(p, base + kScratchPartials, d);
+    p.merge_ways = merge_ways(plan.mode, B, Hkv, v.G, d, P, cus);
     return run_main(p, dtype, d, v.G, plan.mode, s);
 }
 

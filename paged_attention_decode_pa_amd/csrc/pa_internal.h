@@ -73,6 +73,8 @@ struct Params {
     int max_tiles;        // max_blocks * block_size / 16
     int part_tiles_log2;  // a sequence of n tiles uses min(P, ceil(n / 2^this)) partitions,
     int solo_tiles;       // or one when n <= solo_tiles
+    int merge_ways;       // fused merge shared by the last 1, 2 or 4 arrivals (1 unless
+                          // every workgroup of the launch can be resident at once)
     float qk_scale;       // scale * log2(e)
 };
 
@@ -104,6 +106,17 @@ constexpr bool shape_built(int dtype, int d, int G) {
 #define PA_TICKET_STRIDE 32
 #endif
 constexpr int kTicketStride = PA_TICKET_STRIDE;
+
+// Workgroups that share a fused merge (p.merge_ways) when a launch's
+// workgroups can all be resident at once (at most one per compute unit).
+#ifndef PA_MERGE_WAYS
+#define PA_MERGE_WAYS 4
+#endif
+constexpr int kMergeWays = PA_MERGE_WAYS;
+// Rounds a merger waits for the generation of its ticket to move on before it
+// writes NaN instead (a launch whose workgroups cannot all be resident; never
+// reached otherwise).
+constexpr int kMaxPollRounds = 1 << 22;
 
 // Sequences per decode launch: the grid's y extent.
 constexpr int kMaxGridY = 65535;

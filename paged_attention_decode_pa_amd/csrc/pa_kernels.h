@@ -578,26 +578,32 @@ constexpr bool kOrderedTicket = PA_ORDERED_TICKET != 0;
 // have rewritten since.
 constexpr int kCoherent = 16;
 
-// The fused merge of the `busy` partitions of (b, kvh) by one workgroup.  Each
-// (head, 4-element quad) of the group's output is shared by S threads; thread
-// `split` folds partitions split, split + S, ... (all of a chunk's loads in
-// flight at once), then the S partial states are folded together with an xor
-// butterfly, all with the rescale-and-sum rule.  S is chosen so that the
-// items fill the workgroup, which keeps each thread's loads few enough to
-// leave in one round trip; CH (the chunk) is the smallest power of two up to
-// 16 that holds a thread's share, so few partitions load no padding.
-template <int DT, int D, int G, int NW>
+// The fused merge of the `busy` partitions of (b, kvh), or of one of WAYS
+// slices of its head dim (columns [slice * D / WAYS, (slice + 1) * D / WAYS)),
+// by one workgroup.  Each (head, 4-element quad) of the slice is shared by S
+// threads; thread `split` folds partitions split, split + S, ... (all of a
+// chunk's loads in flight at once), then the S partial states are folded
+// together with an xor butterfly, all with the rescale-and-sum rule.  S is
+// chosen so that the items fill the workgroup, which keeps each thread's
+// loads few enough to leave in one round trip; CH (the chunk) is the smallest
+// power of two up to 16 that holds a thread's share, so few partitions load
+// no padding.  Every element's fold order is fixed, so the output bits do not
+// depend on which workgroups merge.  If `poisoned`, the slice is written as
+// NaN instead (a merger that stopped waiting).
+template <int DT, int D, int G, int NW, int WAYS = 1>
 constexpr int merge_split() {
-    constexpr int kThreads = NW * kWave, kItems = G * D / 4;
+    constexpr int kThreads = NW * kWave, kItems = G * D / (4 * WAYS);
     return kItems >= kThreads ? 1 : kThreads / kItems;
 }
 
-template <int DT, int D, int G, int NW, int CH>
-__device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int kvh, int busy) {
+template <int DT, int D, int G, int NW, int CH, int WAYS>
+__device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int kvh, int busy,
+                                                    int slice, bool poisoned) {
     constexpr int kThreads = NW * kWave;
-    constexpr int kQuads = D / 4;
+    constexpr int kQuads = D / (4 * WAYS);
     constexpr int kItems = G * kQuads;
-    constexpr int S = merge_split<DT, D, G, NW>();
+    constexpr int S = merge_split<DT, D, G, NW, WAYS>();
+    static_assert(S <= kWave, "the butterfly stays inside a wave");
     static_assert(kItems % kThreads == 0 || kItems * S == kThreads,
                   "every thread must take part in the butterfly");
     const long long bh0 = (long long)b * p.H + kvh * G;
@@ -607,7 +613,7 @@ __device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int 
         buffer_rsrc(reinterpret_cast<const char *>(p.part_acc + bh0 * p.P * D), G * p.P * D * 4);
     for (int t = threadIdx.x; t < kItems * S; t += kThreads) {
         const int item = t / S, split = t % S;
-        const int h = item / kQuads, quad = item % kQuads;
+        const int h = item / kQuads, quad = slice * kQuads + item % kQuads;
         float M = kMaxInit, L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
         for (int q0 = split; q0 < busy; q0 += S * CH) {
             float2 sm[CH];
@@ -645,7 +651,7 @@ __device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int 
             M = mn;
         }
         if (split == 0) {
-            const float inv = L > 0.f ? 1.f / L : 0.f;
+            const float inv = poisoned ? __builtin_nanf("") : (L > 0.f ? 1.f / L : 0.f);
             const long long at = (bh0 + h) * D + 4 * quad;
             store_pair<DT>(p.out, at, o[0] * inv, o[1] * inv);
             store_pair<DT>(p.out, at + 2, o[2] * inv, o[3] * inv);
@@ -653,15 +659,24 @@ __device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int 
     }
 }
 
-template <int DT, int D, int G, int NW>
-__device__ __forceinline__ void merge_group(const Params &p, int b, int kvh, int busy) {
-    constexpr int S = merge_split<DT, D, G, NW>();
+template <int DT, int D, int G, int NW, int WAYS>
+__device__ __forceinline__ void merge_group_ways(const Params &p, int b, int kvh, int busy,
+                                                 int slice, bool poisoned) {
+    constexpr int S = merge_split<DT, D, G, NW, WAYS>();
     const int share = (busy + S - 1) / S;  // partitions per thread
-    if (share <= 1) merge_group_chunked<DT, D, G, NW, 1>(p, b, kvh, busy);
-    else if (share <= 2) merge_group_chunked<DT, D, G, NW, 2>(p, b, kvh, busy);
-    else if (share <= 4) merge_group_chunked<DT, D, G, NW, 4>(p, b, kvh, busy);
-    else if (share <= 8) merge_group_chunked<DT, D, G, NW, 8>(p, b, kvh, busy);
-    else merge_group_chunked<DT, D, G, NW, 16>(p, b, kvh, busy);
+    if (share <= 1) merge_group_chunked<DT, D, G, NW, 1, WAYS>(p, b, kvh, busy, slice, poisoned);
+    else if (share <= 2) merge_group_chunked<DT, D, G, NW, 2, WAYS>(p, b, kvh, busy, slice, poisoned);
+    else if (share <= 4) merge_group_chunked<DT, D, G, NW, 4, WAYS>(p, b, kvh, busy, slice, poisoned);
+    else if (share <= 8) merge_group_chunked<DT, D, G, NW, 8, WAYS>(p, b, kvh, busy, slice, poisoned);
+    else merge_group_chunked<DT, D, G, NW, 16, WAYS>(p, b, kvh, busy, slice, poisoned);
+}
+
+template <int DT, int D, int G, int NW>
+__device__ __forceinline__ void merge_group(const Params &p, int b, int kvh, int busy, int ways,
+                                            int slice, bool poisoned) {
+    if (ways == 4) merge_group_ways<DT, D, G, NW, 4>(p, b, kvh, busy, slice, poisoned);
+    else if (ways == 2) merge_group_ways<DT, D, G, NW, 2>(p, b, kvh, busy, slice, poisoned);
+    else merge_group_ways<DT, D, G, NW, 1>(p, b, kvh, busy, 0, poisoned);
 }
 
 template <int DT, int D, int G, int NW, int DEPTH, int MODE>
@@ -953,9 +968,15 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
-        // Publish this partition and take a ticket; the last of the VS * `busy`
-        // workgroups of (b, kvh) merges their partitions and resets the ticket
-        // for the next call.
+        // Publish this partition and take a ticket.  The ticket of (b, kvh)
+        // is 64 bits, an arrival count (low half) and a generation (high
+        // half).  Of the n = VS * busy workgroups, the last to arrive (count
+        // n - 1) resets the count and moves the generation on with one
+        // atomic add, and merges; with p.merge_ways = K > 1 the K - 1 before
+        // it (counts n - K .. n - 2) merge too, each its own slice of the
+        // head dim, once they see the generation move on (a bounded wait on
+        // the ticket's line).  K > 1 only when every workgroup of the launch
+        // can be resident at once, so the ones they wait for are running.
         //
         // Ordering (PA_ORDERED_TICKET = 0, the library): the partial sums are
         // agent-scope atomic stores, which on this part write through to the
@@ -963,45 +984,67 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         // once each of this wave's stores is acknowledged there, and the
         // barrier holds thread 0 until all four waves have passed theirs.  The
         // ticket is an agent-scope atomic, performed at that same level and
-        // issued after the barrier, so when any workgroup's ticket reads
-        // VS * busy - 1 the stores behind every earlier ticket are already
-        // there.  The merger issues its loads after its ticket has returned,
-        // with the coherent cache policy (kCoherent), which reads past a stale
-        // L2 copy.  This rests on the cache policy of the stores and loads and
-        // on where atomics are performed, not on the HIP memory model: in the
-        // model the relaxed ticket orders nothing.
+        // issued after the barrier, so when a workgroup's ticket reads n - 1
+        // the stores behind every earlier ticket are already there, and so
+        // they are when a waiting merger reads the moved-on generation, which
+        // the last arrival writes after its own ticket.  Mergers issue their
+        // loads after that, with the coherent cache policy (kCoherent), which
+        // reads past a stale L2 copy.  This rests on the cache policy of the
+        // stores and loads and on where atomics are performed, not on the HIP
+        // memory model: in the model the relaxed ticket orders nothing.
         //
         // PA_ORDERED_TICKET = 1 (the ablation library libpa_decode_ordered.so)
         // orders the same exchange within the memory model: thread 0's ticket
         // is an agent-scope release read-modify-write, so every thread's
         // stores, sequenced before the barrier that synchronises the
-        // workgroup with thread 0, happen before it; the tickets of one
-        // (b, kvh) form a release sequence, so in the workgroup whose ticket
-        // reads VS * busy - 1 the agent-scope acquire fence that follows makes
-        // every other workgroup's stores happen before it, and through the
-        // second barrier before every thread's merge loads.  On gfx950 the
-        // release is an L2 writeback in every publishing workgroup, which
-        // queues: measured +1.2 us on one 16384-token sequence (256
+        // workgroup with thread 0, happen before it.  The tickets of (b, kvh)
+        // and the last arrival's reset form a release sequence of every one
+        // of them, so a merger's agent-scope acquire fence -- after its own
+        // ticket read n - 1, or after it read the moved-on generation --
+        // makes every other workgroup's stores happen before it, and through
+        // the second barrier before every thread's merge loads.  On gfx950
+        // the release is an L2 writeback in every publishing workgroup,
+        // which queues: measured +1.2 us on one 16384-token sequence (256
         // workgroups) and +47 % on a batch of 32 x 8192 tokens (2048).
-        __shared__ int sm_last;
+        __shared__ int sm_role, sm_ways, sm_poisoned;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
-            int *ticket = p.counters + (long long)kTicketStride * (b * p.Hkv + kvh);
-            const int prev = __hip_atomic_fetch_add(
-                ticket, 1, kOrderedTicket ? __ATOMIC_RELEASE : __ATOMIC_RELAXED,
+            auto *ticket = reinterpret_cast<unsigned long long *>(
+                p.counters + (long long)kTicketStride * (b * p.Hkv + kvh));
+            const int n = VS * busy;
+            const int ways = p.merge_ways < n ? p.merge_ways : n;
+            const unsigned long long old = __hip_atomic_fetch_add(
+                ticket, 1ull, kOrderedTicket ? __ATOMIC_RELEASE : __ATOMIC_RELAXED,
                 __HIP_MEMORY_SCOPE_AGENT);
-            const bool last = prev == VS * busy - 1;
-            if (kOrderedTicket && last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            sm_last = last;
+            const int count = (int)(unsigned)(old & 0xFFFFFFFFull);
+            const unsigned gen = (unsigned)(old >> 32);
+            int role = -1, poisoned = 0;
+            if (count == n - 1) {
+                if (kOrderedTicket) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                __hip_atomic_fetch_add(ticket, (1ull << 32) - (unsigned long long)n,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                role = ways - 1;
+            } else if (count >= n - ways) {
+                int rounds = 0;
+                while ((unsigned)(__hip_atomic_load(ticket, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) >> 32) == gen) {
+                    if (++rounds >= kMaxPollRounds) {
+                        poisoned = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (kOrderedTicket) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                role = count - (n - ways);
+            }
+            sm_role = role;
+            sm_ways = ways;
+            sm_poisoned = poisoned;
         }
         __syncthreads();
-        if (sm_last) {
-            merge_group<DT, D, G, NW>(p, b, kvh, busy);
-            if (threadIdx.x == 0)
-                __hip_atomic_store(p.counters + (long long)kTicketStride * (b * p.Hkv + kvh), 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (sm_role >= 0)
+            merge_group<DT, D, G, NW>(p, b, kvh, busy, sm_ways, sm_role, sm_poisoned != 0);
     }
 }
 

@@ -1084,3 +1084,32 @@ def test_uniform_lengths_hint(gpu, lens):
     assert_close(to_f64(out), oracle.decode_case(case), "bf16", "uniform hint")
     single = run_gpu(case, gpu, num_partitions=1)
     assert torch.equal(out, single)
+
+
+SHARED_MERGE_CASES = [
+    # (B, ctx, H, Hkv, d): a fused split whose (sequence, kv head) units hold
+    # at least 48 KiB of partial sums, with at most one workgroup per CU, so
+    # that the last 4 arrivals of each unit share its merge, one quarter of
+    # the head dim each (G = 4, 16, 1 and 4; head dims 128, 128, 256, 64)
+    (1, 16384, 32, 8, 128),
+    (1, 8192, 16, 1, 128),
+    (1, 12000, 4, 4, 256),
+    (1, 30000, 8, 2, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", SHARED_MERGE_CASES, ids=lambda s: f"H{s[2]}_Hkv{s[3]}_d{s[4]}")
+def test_shared_merge(gpu, dtype, shape):
+    B, ctx, H, Hkv, d = shape
+    if not pa_shape_built(dtype, d, H // Hkv):
+        pytest.skip("shape not built")
+    case = pi.make_case(B, ctx - 37, H, Hkv, d, 16, dtype=dtype, seed=ctx + H + d)
+    cus = pa.pa_device_num_cus(0)
+    P, vs = pa.pa_plan(B, Hkv, d, case.max_blocks, 16, cus)
+    assert P > 1 and B * Hkv * P * vs <= cus and P * (H // Hkv) * d * 4 >= 48 << 10
+    say(f"shared merge {dtype} H={H} Hkv={Hkv} d={d} ctx={ctx - 37} P={P} v_slices={vs}")
+    a = run_gpu(case, gpu)
+    assert_close(to_f64(a), oracle.decode_case(case), dtype, f"shared merge P={P}")
+    b = run_gpu(case, gpu)
+    assert torch.equal(a, b), "the shared merge repeats bit for bit"
