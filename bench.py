@@ -10,13 +10,15 @@ Timing: inputs are resident in HBM before the timed region.  Each step uses
 the next of N distinct copies of (K/V pool, q, table, lengths, out), N chosen
 so the copies span >= 1 GiB, so the 256 MB Infinity Cache cannot serve a
 step's K/V reads from the previous visit.  W warm-up steps, then REPS (5)
-timed regions of exactly K steps each, recorded by HIP events on the stream
-the kernels run on.  The K steps are captured in HIP graphs (--eager times
-plain launches); an untimed region is enqueued first and the regions follow
-back to back with no host synchronisation between them, so the GPU is busy
-when every start event fires and no launch gap lands inside a region.  The
-rotation runs on across the regions (one graph per starting copy).  value is
-the median region; the minimum is reported beside it.
+timed regions of exactly K steps each.  Each region's K steps are captured in
+a HIP graph of their own (--eager times plain launches) together with a
+one-thread kernel at each end that writes the device clock (s_memrealtime,
+libpa_read_probe.so), so a region's time is what its K steps took on the
+device, without the graph's launch overhead; HIP events recorded around each
+replay on the same stream are reported beside it (us_per_step_events).  An
+untimed region is enqueued first and the regions follow back to back with no
+host synchronisation between them, and the rotation runs on across them.
+value is the median region; the minimum is reported beside it.
 
 Output: one JSON line (rank 0, N = 1).  value = algorithmic bytes per step /
 step time (GB/s); algorithmic bytes = every live K and V row once per kv head
@@ -72,7 +74,8 @@ def parse():
     ap.add_argument("--partitions", type=int, default=0,
                     help="partition count for the timed workload (0 = the heuristic, "
                          "-1 = the heuristic told that all lengths are equal)")
-    ap.add_argument("--variant", default=None, choices=["valu_qk", "no_vsplit", "ordered"],
+    ap.add_argument("--variant", default=None,
+                    choices=["valu_qk", "no_vsplit", "ordered", "timeline"],
                     help="time an ablation build instead of the library: valu_qk runs the "
                          "q.K product on the vector ALUs instead of the matrix cores; "
                          "no_vsplit never splits V's head dim over two workgroups; ordered "
@@ -83,16 +86,20 @@ def parse():
                     help="timed regions of --steps steps each (median reported)")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the plain streaming-read leg")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the bench line, the per-workgroup timeline of the timed "
+                         "workload's last graph-replayed step (libpa_decode_timeline.so)")
     ap.add_argument("--leg", default=None, metavar="WORKLOAD:PARTITIONS",
                     help=argparse.SUPPRESS)   # one per-config leg, run as a child process
     ap.add_argument("--sweep", nargs="?", const="design-note", default=None,
-                    choices=["design-note", "ragged", "script", "shapes", "uniform"],
+                    choices=["design-note", "ragged", "script", "shapes", "uniform", "read"],
                     help="instead of the headline, a sweep: design-note (single pass vs split "
                          "over batch 1/4 and KV 512..16384), ragged (long-tailed batches), "
                          "script (the benchmark script's default grid), shapes (the headline "
                          "problem at other head dims, dtypes and block sizes), uniform "
                          "(uniform batches covering the device: heuristic, uniform-lengths "
-                         "hint, single pass)")
+                         "hint, single pass), read (the plain read of the headline's bytes at "
+                         "other launch shapes)")
     return ap.parse_args()
 
 
@@ -179,21 +186,54 @@ class Workload:
         return f"pa_decode_kernel (split, fused merge{v})"
 
 
+_PROBE = None
+
+
+def probe_lib():
+    """libpa_read_probe.so: the plain read and the device-clock stamp."""
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        from paged_attention_decode_pa_amd import build as hip_build
+        if not os.path.exists(hip_build.PROBE_LIB):
+            raise RuntimeError(f"{hip_build.PROBE_LIB} not found: build the package first")
+        lib = ctypes.CDLL(hip_build.PROBE_LIB)
+        lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.pa_probe_read.restype = ctypes.c_int
+        lib.pa_probe_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.pa_probe_stamp.restype = ctypes.c_int
+        _PROBE = lib
+    return _PROBE
+
+
+STAMP_HZ = 100e6  # s_memrealtime
+
+
 def time_region(fn, steps, warmup, use_graph, ncopies, reps=REPS):
     """Seconds per call of fn(i, stream) in each of `reps` regions of exactly
-    `steps` calls.  Call i uses rotation copy i % ncopies; an untimed region
-    goes first and the timed ones follow back to back on one stream with no
-    host synchronisation in between, and the call index runs on across them,
-    so every region starts on a busy GPU and continues the rotation."""
+    `steps` calls, as (device-clock times, event times).  Call i uses rotation
+    copy i % ncopies; an untimed region goes first and the timed ones follow
+    back to back on one stream with no host synchronisation in between, and
+    the call index runs on across them, so every region starts on a busy GPU
+    and continues the rotation.  Each timed region is bracketed twice: by a
+    device-clock stamp kernel at each end, in the same graph as its steps (so
+    the graph's launch overhead falls outside), and by HIP events around the
+    graph replay on the same stream."""
     import torch
+    probe = probe_lib()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    stamps = torch.zeros(2 * reps, dtype=torch.int64, device="cuda")
+    slot = lambda j: stamps.data_ptr() + 8 * j
+
+    def stamp(j, s):
+        if probe.pa_probe_stamp(slot(j), s) != 0:
+            raise RuntimeError("pa_probe_stamp failed")
+
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
     if use_graph:
-        # one graph per starting copy the regions need: region r starts at
-        # call r * steps, i.e. at copy (r * steps) % ncopies
-        ngraphs = ncopies // math.gcd(ncopies, steps)
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
@@ -203,19 +243,23 @@ def time_region(fn, steps, warmup, use_graph, ncopies, reps=REPS):
             for i in range(warmup):
                 fn(i, cap.cuda_stream)
         torch.cuda.synchronize()
-        for gi in range(ngraphs):
+        for r in range(reps + 1):        # region 0 is the untimed lead
             g = torch.cuda.CUDAGraph()
             with torch.cuda.stream(cap):
                 g.capture_begin()
+                if r > 0:
+                    stamp(2 * (r - 1), cap.cuda_stream)
                 for i in range(steps):
-                    fn(gi * steps + i, cap.cuda_stream)
+                    fn(r * steps + i, cap.cuda_stream)
+                if r > 0:
+                    stamp(2 * (r - 1) + 1, cap.cuda_stream)
                 g.capture_end()
             graphs.append(g)
         torch.cuda.synchronize()
-        graphs[0].replay()                 # untimed region 0
+        graphs[0].replay()
         for r, (start, end) in enumerate(events):
             start.record(stream)
-            graphs[(r + 1) % ngraphs].replay()
+            graphs[r + 1].replay()
             end.record(stream)
         torch.cuda.synchronize()
         del graphs
@@ -227,11 +271,16 @@ def time_region(fn, steps, warmup, use_graph, ncopies, reps=REPS):
             fn(i, sh)
         for r, (start, end) in enumerate(events):
             start.record(stream)
+            stamp(2 * r, sh)
             for i in range(steps):
                 fn((r + 1) * steps + i, sh)
+            stamp(2 * r + 1, sh)
             end.record(stream)
         torch.cuda.synchronize()
-    return [a.elapsed_time(b) * 1e-3 / steps for a, b in events]
+    st = stamps.cpu().tolist()
+    dev = [(st[2 * r + 1] - st[2 * r]) / STAMP_HZ / steps for r in range(reps)]
+    ev = [a.elapsed_time(b) * 1e-3 / steps for a, b in events]
+    return dev, ev
 
 
 def summarize(times):
@@ -266,36 +315,52 @@ def measure(case, dev, steps, warmup, use_graph, num_partitions=0, reps=REPS):
     if not ok:
         raise SystemExit(f"{case.name}: parity gate FAILED (max err {max_err:.3e}); "
                          "timing would be meaningless")
-    med, best = summarize(time_region(w.step, steps, warmup, use_graph, w.ncopies, reps))
+    dev, ev = time_region(w.step, steps, warmup, use_graph, w.ncopies, reps)
+    med, best = summarize(dev)
+    w.event_median = summarize(ev)[0]
     return w, med, best, max_err
 
 
-def read_ceiling(dev, nbytes, workgroups, steps, warmup, use_graph, reps=REPS):
+def sweep_read(dev, steps, warmup, use_graph):
+    """The plain streaming read (libpa_read_probe.so) of the headline's bytes
+    at other launch shapes: 256 / 512 / 1024 workgroups of 4 waves, 8 / 16 /
+    32 KB in flight per wave."""
+    import pa_inputs as pi
+    nbytes = pi.make_config_case(5).algorithmic_bytes()
+    points = []
+    for wgs in (256, 512, 1024):
+        for depth in (8, 16, 32):
+            med, best, nb = read_ceiling(dev, nbytes, wgs, steps, warmup, use_graph, depth=depth)
+            points.append(dict(workgroups=wgs, kb_in_flight_per_wave=depth, bytes=nb,
+                               us=round(med * 1e6, 3), us_min=round(best * 1e6, 3),
+                               GBps=round(nb / med / 1e9, 1)))
+            log(f"read {nb} bytes, {wgs} workgroups, {depth} KB per wave: {med * 1e6:.2f} us "
+                f"({nb / med / 1e9:.0f} GB/s)")
+    return dict(metric="plain streaming read us of the headline's bytes by launch shape",
+                unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
+                data="synthetic", points=points)
+
+
+def read_ceiling(dev, nbytes, workgroups, steps, warmup, use_graph, reps=REPS, depth=16):
     """Seconds per launch of a plain streaming read of nbytes (rounded up to
     16 bytes) with the decode kernel's load shape: `workgroups` workgroups of 4
-    waves, 16 KB of non-temporal 16-byte loads in flight per wave, over a
-    rotation of copies spanning >= 1 GiB like the decode step's."""
-    import ctypes
+    waves, `depth` KB of non-temporal 16-byte loads in flight per wave, over a
+    rotation of copies spanning >= 1 GiB like the decode step's (depth: 16-byte
+    loads in flight per lane, i.e. KB per wave)."""
     import torch
-    from paged_attention_decode_pa_amd import build as hip_build
-    if not os.path.exists(hip_build.PROBE_LIB):
-        raise RuntimeError(f"{hip_build.PROBE_LIB} not found: build the package first")
-    lib = ctypes.CDLL(hip_build.PROBE_LIB)
-    lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
-                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.pa_probe_read.restype = ctypes.c_int
+    lib = probe_lib()
     nbytes = (nbytes + 15) // 16 * 16
     ncopies = rotation_copies(nbytes)
     bufs = [torch.zeros(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(ncopies)]
     sink = torch.zeros(workgroups, dtype=torch.int32, device=dev)
 
     def fn(i, stream):
-        rc = lib.pa_probe_read(bufs[i % ncopies].data_ptr(), nbytes, workgroups, 16,
+        rc = lib.pa_probe_read(bufs[i % ncopies].data_ptr(), nbytes, workgroups, depth,
                                sink.data_ptr(), stream)
         if rc != 0:
             raise RuntimeError(f"pa_probe_read failed: {rc}")
 
-    med, best = summarize(time_region(fn, steps, warmup, use_graph, ncopies, reps))
+    med, best = summarize(time_region(fn, steps, warmup, use_graph, ncopies, reps)[0])
     del bufs
     torch.cuda.empty_cache()
     return med, best, nbytes
@@ -598,6 +663,64 @@ def sweep(dev, steps, warmup, use_graph):
         crossover_kv_len=crossover, points=points)
 
 
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def timeline(case, dev, steps, warmup, use_graph, parts):
+    """The per-workgroup stamps of the last step of the timed regions, from
+    the timeline library (include/pa_timeline.h), summarised in microseconds
+    from the first workgroup's entry."""
+    import ctypes
+    import torch
+    import paged_attention_decode_pa_amd as pa
+    lib = pa.load_variant("timeline")
+    lib.pa_timeline_enable.argtypes = [ctypes.c_int]
+    lib.pa_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    cap = 1 << 16
+    if lib.pa_timeline_enable(cap) != 0:
+        raise RuntimeError("pa_timeline_enable failed")
+    w, med, best, err = measure(case, dev, steps, warmup, use_graph, parts, reps=1)
+    torch.cuda.synchronize()
+    c = w.case
+    nwg = c.num_kv_heads * c.batch * w.P * w.v_slices
+    if nwg > cap:
+        raise SystemExit(f"{nwg} workgroups: more than the timeline keeps")
+    st = np.zeros(nwg * 16, dtype=np.uint64)
+    if lib.pa_timeline_copy(st.ctypes.data, nwg) != 0:
+        raise RuntimeError("pa_timeline_copy failed")
+    st = st.reshape(nwg, 16).astype(np.int64)
+    t0 = st[:, 0].min()
+    us = lambda x: (x - t0) * 0.01
+    loop_end = us(st[:, 1:5].max(axis=1))
+    kind = st[:, 12]
+    pub = kind == 2
+    role = st[:, 8] & 0xFF
+    merger = role > 0
+    xcc = st[:, 10] & 0xF
+    q = lambda xs: dict(min=round(float(min(xs)), 2), median=round(float(pct(xs, 0.5)), 2),
+                        p90=round(float(pct(xs, 0.9)), 2), max=round(float(max(xs)), 2))
+    out = dict(workload=c.name, partitions=w.P, v_slices=w.v_slices, workgroups=nwg,
+               us_per_step_timeline_build=round(med * 1e6, 3), max_abs_err=err,
+               entry=q(us(st[:, 0])), loop_end=q(loop_end),
+               per_xcd_loop_end_median={int(x): round(float(pct(loop_end[xcc == x], 0.5)), 2)
+                                        for x in sorted(set(xcc.tolist()))})
+    if pub.any():
+        out["loop_end_to_published"] = q((us(st[pub, 6]) - loop_end[pub]).tolist())
+        out["published_to_ticket"] = q((us(st[pub, 7]) - us(st[pub, 6])).tolist())
+    if merger.any():
+        last = merger & (role == ((st[:, 8] >> 40) & 0xFF))
+        out["mergers"] = int(merger.sum())
+        out["merge"] = q((us(st[merger, 9]) - us(st[merger, 7])).tolist())
+        out["last_arrival_ticket"] = q(us(st[last, 7]).tolist())
+        out["step_end"] = round(float(us(st[merger, 9]).max()), 2)
+    else:
+        out["step_end"] = round(float(loop_end.max()), 2)
+    del w
+    return out
+
+
 def leg_row(cid, parts, dev, steps, warmup, use_graph, reps):
     """One per-config leg: workload cid at partition count parts (0 = the
     heuristic), parity-gated and timed like the headline."""
@@ -663,7 +786,7 @@ def child_legs(args, plan, python=None):
 def main():
     global VARIANT
     args = parse()
-    VARIANT = args.variant
+    VARIANT = "timeline" if args.timeline else args.variant
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step has no multi-GPU path in this library)", file=sys.stderr)
@@ -709,7 +832,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.sweep:
         fn = {"design-note": sweep, "ragged": sweep_ragged, "script": sweep_script,
-              "shapes": sweep_shapes, "uniform": sweep_uniform}[args.sweep]
+              "shapes": sweep_shapes, "uniform": sweep_uniform, "read": sweep_read}[args.sweep]
         print(json.dumps(fn(dev, min(args.steps, 500), args.warmup, use_graph)), flush=True)
         return
 
@@ -720,6 +843,11 @@ def main():
                                 name=f"{dt} B={B} ctx={ctx} H={H} Hkv={Hkv} d={d} bs={bs}")
     else:
         headline = pi.make_config_case(args.workload)
+
+    if args.timeline:
+        print(json.dumps(timeline(headline, dev, min(args.steps, 200), args.warmup, use_graph,
+                                  args.partitions)), flush=True)
+        return
 
     w, t_step, t_min, err = measure(headline, dev, args.steps, args.warmup, use_graph,
                                     args.partitions, args.reps)
@@ -734,6 +862,7 @@ def main():
     c = w.case
     grid = c.num_kv_heads * c.batch * w.P * w.v_slices
     ncopies, P, v_slices, kname = w.ncopies, w.P, w.v_slices, w.kernel_name()
+    t_events = w.event_median
     del w
     torch.cuda.empty_cache()
 
@@ -789,6 +918,7 @@ def main():
         "ms_per_step": round(t_step * 1e3, 6),
         "us_per_step": round(t_step * 1e6, 3),
         "us_min": round(t_min * 1e6, 3),
+        "us_per_step_events": round(t_events * 1e6, 3),
         "reps": args.reps,
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
@@ -804,9 +934,12 @@ def main():
             "head_dim": c.head_dim, "block_size": c.block_size,
             "pool_blocks": c.num_pool_blocks, "num_partitions": P, "v_slices": v_slices,
             "algorithmic_bytes_per_step": dom_bytes, "rotation_copies": ncopies,
-            "timing": (f"median of {args.reps} regions of {args.steps} steps, replayed back to "
-                       "back from HIP graphs" if use_graph else
-                       f"median of {args.reps} regions of {args.steps} eager steps"),
+            "timing": (f"median of {args.reps} regions of {args.steps} steps, each a HIP graph "
+                       "replayed back to back with the others and timed by device-clock "
+                       "stamps captured at its two ends (HIP events around the replays in "
+                       "us_per_step_events)" if use_graph else
+                       f"median of {args.reps} regions of {args.steps} eager steps, timed by "
+                       "device-clock stamps at their two ends"),
             "parallelism": "single GPU",
         },
         "roofline": roofline,

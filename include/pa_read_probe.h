@@ -29,6 +29,17 @@ extern "C" {
 int pa_probe_read(const void *src, long long bytes, int workgroups, int depth, unsigned *sink,
                   void *stream);
 
+/*
+ * pa_probe_stamp enqueues on `stream` a one-thread kernel that writes the
+ * device's constant-rate clock (s_memrealtime, a 100 MHz counter shared by
+ * the compute units) to dst[0] (device memory).  Captured at the two ends of a
+ * sequence of steps in one HIP graph, the difference of two stamps is the
+ * time those steps took on the device, without the graph's launch overhead
+ * that events recorded around the graph would include.  Returns 0, -1 (NULL)
+ * or -7 (launch failed).
+ */
+int pa_probe_stamp(unsigned long long *dst, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

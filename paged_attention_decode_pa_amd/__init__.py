@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 # Ablation builds of the same sources (see build.py), loaded only on request.
 VARIANT_PATHS = {"valu_qk": os.path.join(HERE, "libpa_decode_valu_qk.so"),
                  "no_vsplit": os.path.join(HERE, "libpa_decode_no_vsplit.so"),
-                 "ordered": os.path.join(HERE, "libpa_decode_ordered.so")}
+                 "ordered": os.path.join(HERE, "libpa_decode_ordered.so"),
+                 "timeline": os.path.join(HERE, "libpa_decode_timeline.so")}
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1

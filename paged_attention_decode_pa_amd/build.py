@@ -13,7 +13,9 @@ matrix cores; bench.py --variant valu_qk) and libpa_decode_no_vsplit.so
 bench.py --variant no_vsplit).  A third, libpa_decode_ordered.so
 (PA_ORDERED_TICKET=1), orders the fused merge's exchange of partial sums by
 release / acquire in the memory model instead of by cache policy (bench.py
---variant ordered); it computes the same bits.  All else is identical.
+--variant ordered); it computes the same bits.  libpa_decode_timeline.so
+(PA_TIMELINE=1) writes per-workgroup time stamps (include/pa_timeline.h;
+bench.py --timeline).  All else is identical.
 
 libpa_read_probe.so (csrc/pa_read_probe.hip, include/pa_read_probe.h) is a
 plain streaming read with the decode kernel's load shape, the ceiling
@@ -41,6 +43,7 @@ VARIANTS = {
                   SOURCES[:1]),
     "ordered": (os.path.join(HERE, "libpa_decode_ordered.so"), ["-DPA_ORDERED_TICKET=1"],
                 KERNEL_SOURCES),
+    "timeline": (os.path.join(HERE, "libpa_decode_timeline.so"), ["-DPA_TIMELINE=1"], SOURCES),
 }
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

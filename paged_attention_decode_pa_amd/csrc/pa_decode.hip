@@ -13,6 +13,7 @@
 
 #include "pa_decode.h"
 #include "pa_internal.h"
+#include "pa_timeline.h"
 
 namespace {
 
@@ -49,6 +50,13 @@ constexpr int kShortTableTiles = 32;
 bool use_split_v(int d) { return PA_SPLIT_V != 0 && split_v_built(d); }
 
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+#ifndef PA_TIMELINE
+#define PA_TIMELINE 0
+#endif
+// The timeline build's stamp buffer (pa_timeline_enable); null otherwise.
+unsigned long long *g_timeline = nullptr;
+unsigned g_timeline_cap = 0;
 
 // Workspace layout: [B][H][P] float2 (max, sum) | [B][H][P][d] float partial
 // sums, the second region starting on a 256-byte boundary.
@@ -270,6 +278,8 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.part_tiles_log2 = 0;  // every partition up to min(n, P) busy
     p.solo_tiles = 0;
     p.merge_ways = 1;
+    p.timeline = g_timeline;
+    p.timeline_cap = g_timeline_cap;
     p.max_tiles = table_tiles(max_blocks, block_size);
     p.qk_scale = scale * kLog2e;
     return p;
@@ -615,6 +625,32 @@ int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, 
     return run_merge(out, const_cast<void *>(workspace), B, H, P, d, dtype,
                      static_cast<hipStream_t>(stream));
 }
+
+#if PA_TIMELINE
+int pa_timeline_enable(int workgroups) {
+    if (workgroups <= 0) return PA_ERR_VALUE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_timeline && (hipDeviceSynchronize() != hipSuccess || hipFree(g_timeline) != hipSuccess))
+        return PA_ERR_HIP;
+    g_timeline = nullptr;
+    g_timeline_cap = 0;
+    const size_t bytes = (size_t)workgroups * kTimelineSlots * sizeof(unsigned long long);
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, bytes) != hipSuccess) return PA_ERR_HIP;
+    if (hipMemset(ptr, 0, bytes) != hipSuccess) return PA_ERR_HIP;
+    g_timeline = static_cast<unsigned long long *>(ptr);
+    g_timeline_cap = (unsigned)workgroups;
+    return PA_OK;
+}
+
+int pa_timeline_copy(unsigned long long *host, int workgroups) {
+    if (!host) return PA_ERR_NULL;
+    if (workgroups <= 0 || (unsigned)workgroups > g_timeline_cap) return PA_ERR_VALUE;
+    const size_t bytes = (size_t)workgroups * kTimelineSlots * sizeof(unsigned long long);
+    return hipMemcpy(host, g_timeline, bytes, hipMemcpyDeviceToHost) == hipSuccess ? PA_OK
+                                                                                   : PA_ERR_HIP;
+}
+#endif
 
 void pa_release(void) {
     std::lock_guard<std::mutex> lock(g_mutex);

@@ -76,7 +76,14 @@ struct Params {
     int merge_ways;       // fused merge shared by the last 1, 2 or 4 arrivals (1 unless
                           // every workgroup of the launch can be resident at once)
     float qk_scale;       // scale * log2(e)
+    // Timeline build only (PA_TIMELINE=1): kTimelineSlots stamps per
+    // workgroup for the first timeline_cap workgroups of a launch; else null.
+    unsigned long long *timeline;
+    unsigned timeline_cap;
 };
+
+// Stamps per workgroup in the timeline build (pa_timeline.h gives the layout).
+constexpr int kTimelineSlots = 16;
 
 struct MergeParams {
     const float2 *part_ml;

@@ -565,6 +565,17 @@ __device__ __forceinline__ float2 merge_partitions(const float2 *ml, const float
     return merge_chunked<32>(ml, acc, P, d);
 }
 
+#ifndef PA_TIMELINE
+#define PA_TIMELINE 0
+#endif
+// Whether the kernel writes per-workgroup time stamps (s_memrealtime, 100 MHz)
+// to p.timeline: 0 in the library, 1 in the timeline library
+// libpa_decode_timeline.so (layout in include/pa_timeline.h).
+constexpr bool kTimeline = PA_TIMELINE != 0;
+__device__ __forceinline__ unsigned long long stamp_now() {
+    return __builtin_amdgcn_s_memrealtime();
+}
+
 #ifndef PA_ORDERED_TICKET
 #define PA_ORDERED_TICKET 0
 #endif
@@ -708,6 +719,17 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     const int lane = threadIdx.x % kWave;
     const int c16 = lane & 15;  // MFMA column / token of the tile for K
     const int g = lane >> 4;    // MFMA row group (its tokens: 4g..4g+3, or g + 4r)
+    unsigned long long *tl = nullptr;  // this workgroup's stamps (timeline build)
+    if constexpr (kTimeline) {
+        const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+        if (p.timeline && lin < p.timeline_cap) tl = p.timeline + (size_t)kTimelineSlots * lin;
+        if (tl && threadIdx.x == 0) {
+            tl[0] = stamp_now();
+            for (int i = 1; i < kTimelineSlots; ++i) tl[i] = 0;
+            tl[10] = __builtin_amdgcn_s_getreg(20 | (3 << 11));   // HW_REG_XCC_ID [3:0]
+            tl[11] = __builtin_amdgcn_s_getreg(4 | (31 << 11));   // HW_REG_HW_ID
+        }
+    }
 
     // Tiles are dealt in runs of DEPTH consecutive tiles (one group) to the
     // busy * NW (partition, wave) lanes in turn: lane L = part * NW + wave
@@ -882,6 +904,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         }
         ++k;
     } while (!idle && first + stride * k < ntiles);  // group k still holds a live tile
+    if constexpr (kTimeline) {
+        if (tl && lane == 0 && wave < 4) tl[1 + wave] = stamp_now();
+    }
 
     // ---- merge the 4 row groups of the wave -----------------------------------
     // The (m, l) of row g and head h sit in the lanes of row g whose column is
@@ -966,6 +991,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         }
     }
 
+    if constexpr (kTimeline) {
+        if (tl && threadIdx.x == 0) tl[12] = silent ? 3 : (direct ? 1 : 2);
+    }
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
         // Publish this partition and take a ticket.  The ticket of (b, kvh)
@@ -1009,6 +1037,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         __shared__ int sm_role, sm_ways, sm_poisoned;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if constexpr (kTimeline) {
+            if (tl && threadIdx.x == 0) tl[6] = stamp_now();
+        }
         if (threadIdx.x == 0) {
             auto *ticket = reinterpret_cast<unsigned long long *>(
                 p.counters + (long long)kTicketStride * (b * p.Hkv + kvh));
@@ -1041,10 +1072,23 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             sm_role = role;
             sm_ways = ways;
             sm_poisoned = poisoned;
+            if constexpr (kTimeline) {
+                if (tl) {
+                    tl[7] = stamp_now();
+                    tl[8] = (unsigned long long)(role + 1) | ((unsigned long long)count << 8) |
+                            ((unsigned long long)ways << 40);
+                }
+            }
         }
         __syncthreads();
         if (sm_role >= 0)
             merge_group<DT, D, G, NW>(p, b, kvh, busy, sm_ways, sm_role, sm_poisoned != 0);
+        if constexpr (kTimeline) {
+            if (sm_role >= 0) {
+                __syncthreads();
+                if (tl && threadIdx.x == 0) tl[9] = stamp_now();
+            }
+        }
     }
 }
 

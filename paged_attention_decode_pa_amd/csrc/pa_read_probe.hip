@@ -3,8 +3,10 @@
 // load shape (workgroups of 4 waves, 16-byte non-temporal raw buffer loads,
 // 16 KB in flight per wave) and does nothing else: no table, no scores, no
 // merge.  Its time for the bytes one decode step reads is the time no kernel
-// with that load shape can beat on this part.  Built into its own library,
-// libpa_read_probe.so; the decode library does not contain or call it.
+// with that load shape can beat on this part.  Beside it, a one-thread kernel
+// that writes the device clock, which the benchmark captures around its timed
+// steps.  Built into its own library, libpa_read_probe.so; the decode library
+// does not contain or call either.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -56,7 +58,19 @@ __global__ __launch_bounds__(kWaves * kWave) void read_kernel(const char *src, l
     }
 }
 
+// One thread writes the device's constant-rate clock (s_memrealtime, 100 MHz)
+// to dst[0].
+__global__ void stamp_kernel(unsigned long long *dst) {
+    if (threadIdx.x == 0) dst[0] = __builtin_amdgcn_s_memrealtime();
+}
+
 }  // namespace
+
+extern "C" int pa_probe_stamp(unsigned long long *dst, void *stream) {
+    if (!dst) return -1;
+    hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), dst);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
 
 extern "C" int pa_probe_read(const void *src, long long bytes, int workgroups, int depth,
                              unsigned *sink, void *stream) {

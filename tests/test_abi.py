@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pa.EXPORTS)
 
 
-@pytest.mark.parametrize("variant", ["valu_qk", "no_vsplit", "ordered"])
+@pytest.mark.parametrize("variant", ["valu_qk", "no_vsplit", "ordered", "timeline"])
 def test_ablation_library_exports_the_same_functions(variant):
     lib = pa.load_variant(variant)
     for name in declared_functions():
@@ -312,7 +312,7 @@ def test_read_probe_library_exports_its_header():
     text = open(os.path.join(os.path.dirname(HEADER), "pa_read_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
-    assert names == ["pa_probe_read"]
+    assert names == ["pa_probe_read", "pa_probe_stamp"]
     lib = ctypes.CDLL(hip_build.PROBE_LIB)
     fn = lib.pa_probe_read
     fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
@@ -322,6 +322,8 @@ def test_read_probe_library_exports_its_header():
     assert fn(16, -1, 4, 16, 16, None) == -2
     assert fn(16, 1024, 0, 16, 16, None) == -2
     assert fn(16, 1024, 4, 12, 16, None) == -3
+    lib.pa_probe_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.pa_probe_stamp(None, None) == -1
 
 
 
@@ -373,3 +375,21 @@ def test_no_vsplit_ablation_plans_no_v_split():
         ref = pa.pa_plan(B, 8, 128, W, 16, 256, 0)
         if ref[1] == 1:
             assert P.value == ref[0]
+
+
+
+def test_timeline_calls_only_in_the_timeline_library():
+    text = open(os.path.join(os.path.dirname(HEADER), "pa_timeline.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+    assert names == ["pa_timeline_copy", "pa_timeline_enable"]
+    tl = pa.load_variant("timeline")
+    for name in names:
+        assert hasattr(tl, name), name
+        assert not hasattr(pa.load(), name), name
+    import ctypes
+    tl.pa_timeline_enable.argtypes = [ctypes.c_int]
+    tl.pa_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert tl.pa_timeline_enable(0) == pa.PA_ERR_VALUE
+    assert tl.pa_timeline_copy(None, 4) == pa.PA_ERR_NULL
+    assert tl.pa_timeline_copy(16, 4) == pa.PA_ERR_VALUE   # nothing enabled yet

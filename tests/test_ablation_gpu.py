@@ -12,6 +12,9 @@ same arithmetic in the same order.
 libpa_decode_no_vsplit.so (never splits V's head dim): the launches whose V
 split it removes.
 
+libpa_decode_timeline.so (per-workgroup time stamps): the library's exact
+bits, and stamps in causal order.
+
 Their timings only mean something if they compute the same decode step."""
 import ctypes
 import math
@@ -109,3 +112,38 @@ def test_no_vsplit_build(gpu, B, lens):
     say(f"no_vsplit B={B}")
     out = run_variant(case, gpu, 0, variant="no_vsplit")
     assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"no_vsplit B={B}")
+
+
+def test_timeline_build(gpu):
+    # the stamps change no arithmetic, and they come in causal order: entry
+    # <= end of streaming <= published <= ticket <= end of merge, with the
+    # last arrival of every (sequence, kv head) among the mergers
+    tl = pa.load_variant("timeline")
+    tl.pa_timeline_enable.argtypes = [ctypes.c_int]
+    tl.pa_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    case = pi.make_config_case(5)
+    assert tl.pa_timeline_enable(4096) == 0
+    say("timeline build, workload 5")
+    out = run_variant(case, gpu, 0, variant="timeline")
+    ref = run_variant(case, gpu, 0, variant=None)
+    assert torch.equal(out, ref)
+    P, vs = pa.pa_plan(1, 8, 128, case.max_blocks, 16, pa.pa_device_num_cus(0))
+    n = 8 * P * vs
+    st = np.zeros(16 * n, dtype=np.uint64)
+    assert tl.pa_timeline_copy(st.ctypes.data, n) == 0
+    st = st.reshape(n, 16).astype(np.int64)
+    loop_end = st[:, 1:5].max(axis=1)
+    assert (st[:, 0] > 0).all() and (st[:, 0] <= st[:, 1:5].min(axis=1)).all()
+    assert (st[:, 12] == 2).all()                      # every partition publishes
+    assert (loop_end <= st[:, 6]).all() and (st[:, 6] <= st[:, 7]).all()
+    role = st[:, 8] & 0xFF
+    ways = (st[:, 8] >> 40) & 0xFF
+    count = (st[:, 8] >> 8) & 0xFFFFFFFF
+    merger = role > 0
+    assert (st[merger, 7] <= st[merger, 9]).all()
+    kvh = np.arange(n) % 8
+    for h in range(8):
+        u = kvh == h
+        assert sorted(count[u].tolist()) == list(range(P * vs))  # one ticket each
+        assert merger[u].sum() == ways[u][0]                     # the last `ways` arrivals
+        assert role[u & (count == P * vs - 1)][0] == ways[u][0]  # the last one among them

@@ -42,6 +42,8 @@ def test_bench_prints_one_consistent_json_line(gpu):
     assert c["single_thread"]["value"] > 0
     # median and min of the timed regions; the read ceiling beside the kernel
     assert d["reps"] == 5 and 0 < d["us_min"] <= d["us_per_step"]
+    # device-clock region times exclude the graph launches the events include
+    assert 0 < d["us_per_step"] <= 1.02 * d["us_per_step_events"]
     assert r["read_ceiling_us"] > 0 and r["read_ceiling_bytes"] >= bytes_per_step
     assert abs(r["frac_of_read_ceiling"] - r["read_ceiling_us"] / r["avg_launch_us"]) < 1e-3
 

@@ -29,17 +29,26 @@ def test_no_kernel_uses_scratch():
     assert not bad, f"kernels using scratch: {bad}"
 
 
-def test_valu_qk_ablation_uses_no_scratch():
-    """The ablation build's changed kernels (16-bit) also keep to registers."""
-    _, flags, _ = hip_build.VARIANTS["valu_qk"]
-    srcs = [s for s in hip_build.KERNEL_SOURCES if "f32" not in s]
+def test_ablation_kernels_use_no_scratch():
+    """The ablation builds' changed kernels also keep to registers (the
+    vector-ALU q.K build changes only the 16-bit kernels).  All variants'
+    objects compile in one parallel batch."""
+    import os
     with tempfile.TemporaryDirectory() as tmp:
-        results = hip_build.compile_objects(
-            srcs, tmp, extra=[*flags, "-Rpass-analysis=kernel-resource-usage"])
-    for src, _, rc, err in results:
-        assert rc == 0, err[-2000:]
-        n = re.findall(r"Function Name: (\S+)", err)
-        s = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", err)]
-        assert len(n) == len(s) and n, src
-        bad = [a for a, b in zip(n, s) if b != 0]
-        assert not bad, f"kernels using scratch: {bad}"
+        pending = []
+        for variant in ("valu_qk", "ordered", "timeline"):
+            _, flags, _ = hip_build.VARIANTS[variant]
+            srcs = [x for x in hip_build.KERNEL_SOURCES if variant != "valu_qk" or "f32" not in x]
+            out = os.path.join(tmp, variant)
+            os.mkdir(out)
+            pending.append((variant, hip_build.compile_objects_async(
+                srcs, out, extra=[*flags, "-Rpass-analysis=kernel-resource-usage"])))
+        for variant, procs in pending:
+            for src, _, proc in procs:
+                _, err = proc.communicate()
+                assert proc.returncode == 0, err[-2000:]
+                n = re.findall(r"Function Name: (\S+)", err)
+                sc = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", err)]
+                assert len(n) == len(sc) and n, (variant, src)
+                bad = [a for a, b in zip(n, sc) if b != 0]
+                assert not bad, f"{variant}: kernels using scratch: {bad}"
