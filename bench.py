@@ -79,7 +79,8 @@ def parse():
                     help="time an ablation build instead of the library: valu_qk runs the "
                          "q.K product on the vector ALUs instead of the matrix cores; "
                          "no_vsplit never splits V's head dim over two workgroups; ordered "
-                         "orders the fused merge by release / acquire")
+                         "orders the fused merge by release / acquire; timeline writes "
+                         "per-workgroup stamps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (counter scale)")
     ap.add_argument("--reps", type=int, default=REPS,
@@ -707,13 +708,28 @@ def timeline(case, dev, steps, warmup, use_graph, parts):
                per_xcd_loop_end_median={int(x): round(float(pct(loop_end[xcc == x], 0.5)), 2)
                                         for x in sorted(set(xcc.tolist()))})
     if pub.any():
+        w0_end = us(st[pub, 1])
+        out["wave0_loop_end_to_rows_merged"] = q((us(st[pub, 13]) - w0_end).tolist())
+        out["loop_end_to_waves_in_lds"] = q((us(st[pub, 14]) - loop_end[pub]).tolist())
+        out["waves_in_lds_to_published"] = q((us(st[pub, 6]) - us(st[pub, 14])).tolist())
         out["loop_end_to_published"] = q((us(st[pub, 6]) - loop_end[pub]).tolist())
-        out["published_to_ticket"] = q((us(st[pub, 7]) - us(st[pub, 6])).tolist())
+        out["published_to_acknowledged"] = q((us(st[pub, 15]) - us(st[pub, 6])).tolist())
+        out["acknowledged_to_ticket"] = q((us(st[pub, 7]) - us(st[pub, 15])).tolist())
     if merger.any():
-        last = merger & (role == ((st[:, 8] >> 40) & 0xFF))
+        # per (sequence, kv head) unit: from its last record issued to the end
+        # of its last merger, the part of the step no streaming overlaps
+        unit = np.arange(nwg) % (c.num_kv_heads * c.batch)
+        tails, last_issue = [], []
+        for u in sorted(set(unit[merger].tolist())):
+            m = unit == u
+            li = us(st[m & pub, 6]).max()
+            last_issue.append(li)
+            tails.append(us(st[m & merger, 9]).max() - li)
         out["mergers"] = int(merger.sum())
+        out["merge_ways"] = int(((st[merger, 8] >> 40) & 0xFF).max())
         out["merge"] = q((us(st[merger, 9]) - us(st[merger, 7])).tolist())
-        out["last_arrival_ticket"] = q(us(st[last, 7]).tolist())
+        out["unit_last_record"] = q(last_issue)
+        out["unit_last_record_to_merged"] = q(tails)
         out["step_end"] = round(float(us(st[merger, 9]).max()), 2)
     else:
         out["step_end"] = round(float(loop_end.max()), 2)

@@ -20,7 +20,10 @@
  * s_memrealtime (100 MHz):
  *   0       entry
  *   1 .. 4  end of the streaming loop of waves 0 .. 3
- *   6       partial sums published (after the stores' wait and the barrier)
+ *   13      wave 0's four row groups merged (after its loop)
+ *   14      every wave's sums in LDS (after the barrier)
+ *   6       thread 0's share of the output or of the partial record issued
+ *   15      the record's stores acknowledged (after the wait and the barrier)
  *   7       ticket returned (and, for a waiting merger, the wait ended)
  *   8       bits 0..7: merge role + 1 (0 = does not merge), bits 8..39: the
  *           ticket's arrival count, bits 40..47: workgroups sharing the merge

@@ -944,6 +944,10 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         quarter[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
 
+    if constexpr (kTimeline) {
+        if (tl && threadIdx.x == 0) tl[13] = stamp_now();  // wave 0's rows merged
+    }
+
     // ---- merge the waves through LDS ------------------------------------------
     __shared__ float2 sm_ml[NW][G];
     __shared__ float sm_acc[NW][G][DV];
@@ -957,6 +961,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         for (int h = 0; h < G; ++h) sm_ml[wave][h] = make_float2(mh[h], lh[h]);
     }
     __syncthreads();
+    if constexpr (kTimeline) {
+        if (tl && threadIdx.x == 0) tl[14] = stamp_now();  // every wave in LDS
+    }
 
     // Thread t handles head h = idx / (DV / 2) and elements 2 (idx % (DV / 2)) + {0, 1}
     // of this workgroup's slice.
@@ -992,7 +999,10 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     }
 
     if constexpr (kTimeline) {
-        if (tl && threadIdx.x == 0) tl[12] = silent ? 3 : (direct ? 1 : 2);
+        if (tl && threadIdx.x == 0) {
+            tl[6] = stamp_now();  // thread 0's share of the output or record issued
+            tl[12] = silent ? 3 : (direct ? 1 : 2);
+        }
     }
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
@@ -1038,7 +1048,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if constexpr (kTimeline) {
-            if (tl && threadIdx.x == 0) tl[6] = stamp_now();
+            if (tl && threadIdx.x == 0) tl[15] = stamp_now();  // stores acknowledged
         }
         if (threadIdx.x == 0) {
             auto *ticket = reinterpret_cast<unsigned long long *>(

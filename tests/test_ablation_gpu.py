@@ -116,8 +116,9 @@ def test_no_vsplit_build(gpu, B, lens):
 
 def test_timeline_build(gpu):
     # the stamps change no arithmetic, and they come in causal order: entry
-    # <= end of streaming <= published <= ticket <= end of merge, with the
-    # last arrival of every (sequence, kv head) among the mergers
+    # <= end of streaming <= rows merged <= waves in LDS <= record issued <=
+    # stores acknowledged <= ticket <= end of merge, with the last `ways`
+    # arrivals of every (sequence, kv head) merging, the last one last
     tl = pa.load_variant("timeline")
     tl.pa_timeline_enable.argtypes = [ctypes.c_int]
     tl.pa_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
@@ -135,7 +136,9 @@ def test_timeline_build(gpu):
     loop_end = st[:, 1:5].max(axis=1)
     assert (st[:, 0] > 0).all() and (st[:, 0] <= st[:, 1:5].min(axis=1)).all()
     assert (st[:, 12] == 2).all()                      # every partition publishes
-    assert (loop_end <= st[:, 6]).all() and (st[:, 6] <= st[:, 7]).all()
+    assert (st[:, 1] <= st[:, 13]).all() and (loop_end <= st[:, 14]).all()
+    assert (st[:, 14] <= st[:, 6]).all() and (st[:, 6] <= st[:, 15]).all()
+    assert (st[:, 15] <= st[:, 7]).all()
     role = st[:, 8] & 0xFF
     ways = (st[:, 8] >> 40) & 0xFF
     count = (st[:, 8] >> 8) & 0xFFFFFFFF

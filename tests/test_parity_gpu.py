@@ -1113,3 +1113,47 @@ def test_shared_merge(gpu, dtype, shape):
     assert_close(to_f64(a), oracle.decode_case(case), dtype, f"shared merge P={P}")
     b = run_gpu(case, gpu)
     assert torch.equal(a, b), "the shared merge repeats bit for bit"
+
+
+# Calls on one stream whose fused merges take every path through the library's
+# buffers in turn, each with a layout of its own: a merge shared by the last 4
+# arrivals (one long sequence), the last arrival alone (units of 16 KiB of
+# partials), shared by 4 and by 2 in one launch (a ragged batch whose short
+# sequence has only 2 or 3 partitions), with V split, and with more
+# workgroups than compute units.  Each call must leave its tickets at zero
+# whatever the next call's layout, and no call may take another's partial
+# sums for its own: so every output matches the oracle, and the first shape,
+# run again at the end, repeats bit for bit.
+MERGE_PATH_CASES = [
+    # (B, lens, H, Hkv, d, dtype)
+    (1, [16000], 32, 8, 128, "bf16"),
+    (4, [2048, 1900, 2047, 1500], 32, 8, 128, "bf16"),
+    (2, [16000, 700], 16, 4, 128, "f16"),
+    (1, [700], 32, 8, 128, "f32"),
+    (40, [9000, 300] * 20, 32, 8, 128, "bf16"),
+    (2, [5000, 4100], 16, 2, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("entry", ["pa_decode", "pa_decode_noalloc"])
+def test_merge_paths_back_to_back(gpu, entry):
+    cus = pa.pa_device_num_cus(0)
+    fn = pa.pa_decode if entry == "pa_decode" else pa.pa_decode_noalloc
+    s = torch.cuda.Stream()
+    first = None
+    for i, (B, lens, H, Hkv, d, dtype) in enumerate(MERGE_PATH_CASES + MERGE_PATH_CASES[:1]):
+        case = pi.make_case(B, lens, H, Hkv, d, 16, dtype=dtype, seed=90 + i % len(MERGE_PATH_CASES))
+        P, vs = pa.pa_plan(B, Hkv, d, case.max_blocks, 16, cus)
+        say(f"{entry} merge path {i}: B={B} H={H} Hkv={Hkv} d={d} {dtype} P={P} v_slices={vs} "
+            f"workgroups={B * Hkv * P * vs}")
+        assert P > 1
+        dc = DeviceCase(case, gpu)
+        out = torch.empty_like(dc.q)
+        with torch.cuda.stream(s):
+            fn(out, *dc.args(), s)
+        s.synchronize()
+        assert_close(to_f64(out), oracle.decode_case(case), dtype, f"{entry} path {i}")
+        if i == 0:
+            first = out.clone()
+        elif i == len(MERGE_PATH_CASES):
+            assert torch.equal(out, first), "the first shape again repeats bit for bit"
