@@ -706,7 +706,13 @@ def timeline(case, dev, steps, warmup, use_graph, parts):
                us_per_step_timeline_build=round(med * 1e6, 3), max_abs_err=err,
                entry=q(us(st[:, 0])), loop_end=q(loop_end),
                per_xcd_loop_end_median={int(x): round(float(pct(loop_end[xcc == x], 0.5)), 2)
-                                        for x in sorted(set(xcc.tolist()))})
+                                        for x in sorted(set(xcc.tolist()))},
+               # workgroups dealt to the 8 XCDs round-robin by linear id, from an
+               # XCD that need not be 0: the share of workgroups on XCD
+               # (linear id + the most common offset) mod 8, and that offset
+               xcd_round_robin=round(float(np.bincount((xcc - np.arange(nwg)) % 8,
+                                                        minlength=8).max() / nwg), 4),
+               xcd_offset=int(np.bincount((xcc - np.arange(nwg)) % 8, minlength=8).argmax()))
     if pub.any():
         w0_end = us(st[pub, 1])
         out["wave0_loop_end_to_rows_merged"] = q((us(st[pub, 13]) - w0_end).tolist())
