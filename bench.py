@@ -651,7 +651,10 @@ def sweep(dev, steps, warmup, use_graph):
             points.append(row)
     crossover = {}
     for batch in SWEEP_BATCHES:
-        wins = [p["kv_len"] for p in points if p["batch"] == batch and p["split_speedup"] > 1]
+        # (a point where the heuristic itself runs one partition is the single
+        # pass twice, not a win of the split)
+        wins = [p["kv_len"] for p in points if p["batch"] == batch and p["split_speedup"] > 1
+                and p["split_partitions"] > 1]
         crossover[str(batch)] = min(wins) if wins else None
     return dict(
         metric="decode step us, fused single pass vs split-KV (Flash-Decoding) with fused merge",

@@ -1054,7 +1054,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
             auto *ticket = reinterpret_cast<unsigned long long *>(
                 p.counters + (long long)kTicketStride * (b * p.Hkv + kvh));
             const int n = VS * busy;
-            const int ways = p.merge_ways < n ? p.merge_ways : n;
+            // the largest power of two up to p.merge_ways that n workgroups fill
+            int ways = 1;
+            while (2 * ways <= p.merge_ways && 2 * ways <= n) ways *= 2;
             const unsigned long long old = __hip_atomic_fetch_add(
                 ticket, 1ull, kOrderedTicket ? __ATOMIC_RELEASE : __ATOMIC_RELAXED,
                 __HIP_MEMORY_SCOPE_AGENT);
