@@ -875,8 +875,26 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         if (silent) return;  // nothing in flight touches memory
     }
     if constexpr (MODE == kFusedLate) load_query();
+    // Group k is updated while group k + 1 streams in.  The last group is
+    // peeled off the loop: issuing loads after it (empty, but still a trip
+    // through the load pipeline that the epilogue's use of their registers
+    // would wait for) measured 0.05-0.2 us slower on workloads 1-5, and a
+    // branch around that issue inside the loop slower still.
+    auto update_slot = [&](int s) {
+        if constexpr (kValu)
+            update_tile<DT, D, G, true, DV>(st, tile_scores_rows_valu<DT>(kr[s], qr, g, c16),
+                                        vr[s], p.qk_scale, g, nl[s]);
+        else if constexpr (kRows)
+            update_tile<DT, D, G, true, DV>(st,
+                                        tile_scores_rows<DT, D, kSets>(
+                                            kr[s], qr, c16 / kRowsT, (c16 % G) / kRowsT),
+                                        vr[s], p.qk_scale, g, nl[s]);
+        else
+            update_tile<DT, D, G, false, DV>(st, tile_scores<DT, D>(kr[s], qr), vr[s],
+                                         p.qk_scale, g, nl[s]);
+    };
     int k = 0;
-    do {
+    while (!idle && first + stride * (k + 1) < ntiles) {  // group k + 1 holds a live tile
         const int nbase = first + stride * (k + 1);  // the next group's first tile
         int nid[DEPTH];
 #pragma unroll
@@ -886,24 +904,17 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         // rows as well, since loads complete in order, and measures slower)
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-            if constexpr (kValu)
-                update_tile<DT, D, G, true, DV>(st, tile_scores_rows_valu<DT>(kr[s], qr, g, c16),
-                                            vr[s], p.qk_scale, g, nl[s]);
-            else if constexpr (kRows)
-                update_tile<DT, D, G, true, DV>(st,
-                                            tile_scores_rows<DT, D, kSets>(
-                                                kr[s], qr, c16 / kRowsT, (c16 % G) / kRowsT),
-                                            vr[s], p.qk_scale, g, nl[s]);
-            else
-                update_tile<DT, D, G, false, DV>(st, tile_scores<DT, D>(kr[s], qr), vr[s],
-                                             p.qk_scale, g, nl[s]);
+            update_slot(s);
             nl[s] = live_tokens(nbase + s, nid[s]);
-            // (tiles past the context are issued too, with empty ranges: a
-            // branch here measures slower than the loads it would save)
+            // (a slot of the group past the context is issued too, with an
+            // empty range: a branch here measures slower than the loads it
+            // would save)
             issue(kr[s], vr[s], nbase + s, nid[s], nl[s]);
         }
         ++k;
-    } while (!idle && first + stride * k < ntiles);  // group k still holds a live tile
+    }
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) update_slot(s);  // the last group
     if constexpr (kTimeline) {
         if (tl && lane == 0 && wave < 4) tl[1 + wave] = stamp_now();
     }
