@@ -145,7 +145,8 @@ class Workload:
         self.cus = pa.pa_device_num_cus(dev.index or 0)
         # the launch the library makes: partitions, and V slices per partition
         self.P, self.v_slices = pa.pa_plan(c.batch, c.num_kv_heads, c.head_dim, c.max_blocks,
-                                           c.block_size, self.cus, num_partitions)
+                                           c.block_size, self.cus, num_partitions,
+                                           H=c.num_heads, dtype=self.dtype)
         self.num_partitions = num_partitions
         # every step here uses the library-owned workspace (no caller workspace)
         self.caller_workspace = False

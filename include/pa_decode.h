@@ -35,10 +35,14 @@
  *   - Supported shapes: d in {64, 128, 256} (the benchmark script's head_dim
  *     argument; 128 in every configuration of the docs page); block_size a
  *     power of two from 16 to 256; H % Hkv == 0 with G = H / Hkv in
- *     {1, 2, 4, 8, 16}, except that d = 256 is built only for G <= 8 with
- *     bf16 and fp16 and for G <= 2 with fp32 (the fp32 accumulators of the
- *     other d = 256 groups would not fit the register file); B * H < 2^31;
- *     max_blocks * block_size <= 2^30.  Others return PA_ERR_UNSUPPORTED.
+ *     {1, 2, 4, 8, 16}; B * H < 2^31; max_blocks * block_size <= 2^30;
+ *     16 token rows of one kv head (16 * Hkv * d * element size bytes)
+ *     below 2^31.  Others return PA_ERR_UNSUPPORTED.  With d = 256 and
+ *     G = 16 (bf16, fp16), or G >= 8 (fp32), the fp32 accumulators of a
+ *     whole head row for every head of the group would not fit the register
+ *     file, so those shapes always run with V's head dim split over two
+ *     workgroups (see pa_decode), and with half the heuristic's partitions
+ *     while the units are fewer than the compute units.
  *     Sequences are processed in tiles of 16 tokens; a row of the table
  *     covers T = max_blocks * block_size / 16 tiles.
  *   - All calls only enqueue work on `stream` (a hipStream_t, NULL = the null
@@ -124,7 +128,9 @@ enum {
  * device at once, at most one per compute unit).  When the
  * B * Hkv * P workgroups fill at most a quarter of the compute units (and
  * d >= 128), each partition is again served by two workgroups, one per half
- * of V's head dim, and the ticket counts both.  A sequence
+ * of V's head dim, and the ticket counts both.  The shapes that always split V
+ * (see Supported shapes) do so whatever the launch's size: as the single pass,
+ * the fused split, and the split kernel of a caller workspace.  A sequence
  * with at most one non-empty partition is written directly by partition 0
  * (zeros for an empty sequence); empty partitions do nothing.
  *
@@ -267,12 +273,14 @@ int pa_choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num
  * 0 = heuristic, PA_PARTITIONS_UNIFORM, n > 0 = forced), *v_slices = 2 when
  * each unit (P == 1) or
  * each partition (P > 1) is served by two workgroups, one per half of V's
- * head dim, else 1.  Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (B < 0, Hkv,
- * max_blocks or num_cus <= 0), PA_ERR_VALUE (num_partitions < -1) or
- * PA_ERR_UNSUPPORTED (d or block_size not supported).
+ * head dim, else 1.  H and dtype matter only for the shapes that always split
+ * V (see Supported shapes).  Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (B < 0,
+ * H, Hkv, max_blocks or num_cus <= 0, or H % Hkv != 0), PA_ERR_DTYPE,
+ * PA_ERR_VALUE (num_partitions < -1) or PA_ERR_UNSUPPORTED (d, block_size or
+ * H / Hkv not supported).
  */
-int pa_plan(int B, int Hkv, int d, int max_blocks, int block_size, int num_cus,
-            int num_partitions, int *partitions, int *v_slices);
+int pa_plan(int B, int H, int Hkv, int d, int dtype, int max_blocks, int block_size,
+            int num_cus, int num_partitions, int *partitions, int *v_slices);
 
 /* Compute units of HIP device `device` (cached), or a negative PA_ERR_*. */
 int pa_device_num_cus(int device);

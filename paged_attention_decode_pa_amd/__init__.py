@@ -76,7 +76,7 @@ def load(path: Optional[str] = None):
     lib.pa_workspace_bytes.restype = SZ
     lib.pa_choose_partitions.argtypes = [I, I, I, I, I]
     IP = ctypes.POINTER(ctypes.c_int)
-    lib.pa_plan.argtypes = [I, I, I, I, I, I, I, IP, IP]
+    lib.pa_plan.argtypes = [I, I, I, I, I, I, I, I, I, IP, IP]
     lib.pa_device_num_cus.argtypes = [I]
     lib.pa_strerror.argtypes = [I]
     lib.pa_strerror.restype = ctypes.c_char_p
@@ -186,12 +186,15 @@ def pa_choose_partitions(B, Hkv, max_blocks, block_size, num_cus) -> int:
     return int(load().pa_choose_partitions(B, Hkv, max_blocks, block_size, num_cus))
 
 
-def pa_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions=0):
+def pa_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions=0, H=None,
+            dtype=PA_DTYPE_BF16):
     """(partitions, v_slices) of the launch pa_decode_ex makes without a caller
-    workspace."""
+    workspace.  H (default Hkv) and dtype matter only for the shapes that
+    always split V's head dim (d = 256 with large groups)."""
     P, vs = ctypes.c_int(0), ctypes.c_int(0)
-    _check(load().pa_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions,
-                          ctypes.byref(P), ctypes.byref(vs)), "pa_plan")
+    _check(load().pa_plan(B, Hkv if H is None else H, Hkv, d, dtype, max_blocks, block_size,
+                          num_cus, num_partitions, ctypes.byref(P), ctypes.byref(vs)),
+           "pa_plan")
     return P.value, vs.value
 
 

@@ -9,8 +9,9 @@ design choice brings; the package never loads them by itself:
 libpa_decode_valu_qk.so (PA_QK_VALU=1: the q.K product of the 16-bit,
 head-dim-128, 4-heads-per-kv-head kernels on the vector ALUs instead of the
 matrix cores; bench.py --variant valu_qk) and libpa_decode_no_vsplit.so
-(PA_SPLIT_V=0 in the launcher: never split V's head dim over two workgroups;
-bench.py --variant no_vsplit).  A third, libpa_decode_ordered.so
+(PA_SPLIT_V=0 in the launcher: never split V's head dim over two workgroups
+where it need not, i.e. except for the d = 256 shapes built only with the
+split; bench.py --variant no_vsplit).  A third, libpa_decode_ordered.so
 (PA_ORDERED_TICKET=1), orders the fused merge's exchange of partial sums by
 release / acquire in the memory model instead of by cache policy (bench.py
 --variant ordered); it computes the same bits.  libpa_decode_timeline.so

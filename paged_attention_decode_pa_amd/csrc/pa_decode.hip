@@ -44,9 +44,10 @@ constexpr int kShortTableTiles = 32;
 #define PA_SPLIT_V 1
 #endif
 // Whether the launcher may split V's head dim over two workgroups (the
-// kSingleSplitV and kFusedSplitV modes).  The library is built with 1; the
-// ablation library libpa_decode_no_vsplit.so is built with 0 to measure what
-// the split costs and saves, all else identical.
+// kSingleSplitV and kFusedSplitV modes) where it would not have to.  The
+// library is built with 1; the ablation library libpa_decode_no_vsplit.so is
+// built with 0 to measure what the split costs and saves, all else identical
+// (the shapes built only with V split, v_split_only, split it in both).
 bool use_split_v(int d) { return PA_SPLIT_V != 0 && split_v_built(d); }
 
 size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
@@ -311,7 +312,7 @@ struct Plan {
 int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus);
 
 Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
-               int num_partitions, bool caller_workspace) {
+               int num_partitions, bool caller_workspace, bool split_only) {
     Plan plan{1, kSingle, 0, 0};  // forced counts: every partition up to min(n, P) busy
     const long long units = (long long)B * Hkv;
     const bool covered = units >= cus;
@@ -319,6 +320,10 @@ Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
     if (uniform) num_partitions = 0;
     if (num_partitions == 0) {
         plan.P = choose_partitions(B, Hkv, max_blocks, block_size, cus);
+        // A shape built only with V split runs two workgroups per partition:
+        // half the partitions keep them within the compute units (its kernels
+        // run one workgroup per CU at a time).
+        if (split_only && !covered && plan.P > 1) plan.P /= 2;
         // Two partitions of a short table lose to the single pass with V's
         // head dim split over the same two workgroups per unit, which needs
         // no merge (measured at 96-128 units: at 512 tokens the single pass is
@@ -341,7 +346,9 @@ Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
                                   num_partitions < kMaxPartitions ? num_partitions
                                                                   : kMaxPartitions);
     }
-    if (plan.P == 1) {
+    if (split_only) {
+        plan.mode = plan.P == 1 ? kSingleSplitV : (caller_workspace ? kPartialsSplitV : kFusedSplitV);
+    } else if (plan.P == 1) {
         // A single pass whose units fill at most half of the compute units
         // runs as two workgroups per unit, each with half of V's head dim.
         plan.mode = use_split_v(d) && 2 * units <= cus ? kSingleSplitV : kSingle;
@@ -466,8 +473,7 @@ const char *pa_strerror(int code) {
         case PA_ERR_SHAPE: return "negative or inconsistent sizes";
         case PA_ERR_UNSUPPORTED:
             return "shape not supported (needs d in {64,128,256}, block_size a power of 2 in "
-                   "16..256, H/Hkv in {1,2,4,8,16}; d=256 only with H/Hkv <= 8 for bf16/fp16 "
-                   "and <= 2 for fp32)";
+                   "16..256, H/Hkv in {1,2,4,8,16}, and the size limits of pa_decode.h)";
         case PA_ERR_DTYPE: return "unknown dtype";
         case PA_ERR_ALIGN: return "pointer alignment (16 bytes for tensors, 4 for int32 arrays)";
         case PA_ERR_WORKSPACE:
@@ -500,7 +506,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     const int cus = device_cus(dev);
     if (cus < 0) return cus;
     const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, cus, num_partitions,
-                                workspace != nullptr);
+                                workspace != nullptr, v_split_only(dtype, d, v.G));
     const int P = plan.P;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
@@ -513,7 +519,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
         // caller workspace: split kernel, then the merge kernel (no tickets)
         if (workspace_bytes < need) return PA_ERR_WORKSPACE;
         attach_workspace(p, workspace, d);
-        if ((rc = run_main(p, dtype, d, v.G, kPartials, s)) != PA_OK) return rc;
+        if ((rc = run_main(p, dtype, d, v.G, plan.mode, s)) != PA_OK) return rc;
         return run_merge(out, workspace, B, H, P, d, dtype, s);
     }
     void *ws = nullptr;
@@ -528,15 +534,18 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     return run_main(p, dtype, d, v.G, plan.mode, s);
 }
 
-int pa_plan(int B, int Hkv, int d, int max_blocks, int block_size, int num_cus,
-            int num_partitions, int *partitions, int *v_slices_out) {
+int pa_plan(int B, int H, int Hkv, int d, int dtype, int max_blocks, int block_size,
+            int num_cus, int num_partitions, int *partitions, int *v_slices_out) {
     if (!partitions || !v_slices_out) return PA_ERR_NULL;
-    if (B < 0 || Hkv <= 0 || max_blocks <= 0 || num_cus <= 0) return PA_ERR_SHAPE;
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || max_blocks <= 0 || num_cus <= 0)
+        return PA_ERR_SHAPE;
+    if (!known_dtype(dtype)) return PA_ERR_DTYPE;
     if (num_partitions < PA_PARTITIONS_UNIFORM) return PA_ERR_VALUE;
     if (!supported_head_dim(d) || block_size < kTile || block_size > kMaxBlockSize ||
-        (block_size & (block_size - 1)) != 0)
+        (block_size & (block_size - 1)) != 0 || !shape_built(dtype, d, H / Hkv))
         return PA_ERR_UNSUPPORTED;
-    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions, false);
+    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, num_cus, num_partitions, false,
+                                v_split_only(dtype, d, H / Hkv));
     *partitions = plan.P;
     *v_slices_out = v_slices(plan.mode);
     return PA_OK;
@@ -563,7 +572,8 @@ int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void 
     if ((rc = current_device(&dev)) != PA_OK) return rc;
     const int cus = device_cus(dev);
     if (cus < 0) return cus;
-    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, cus, 0, false);
+    const Plan plan = make_plan(B, Hkv, d, max_blocks, block_size, cus, 0, false,
+                                v_split_only(dtype, d, v.G));
     const int P = plan.P;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, 0, P);
@@ -603,7 +613,8 @@ int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
     attach_workspace(p, workspace, d);
-    return run_main(p, dtype, d, v.G, kPartials, static_cast<hipStream_t>(stream));
+    return run_main(p, dtype, d, v.G, v_split_only(dtype, d, v.G) ? kPartialsSplitV : kPartials,
+                    static_cast<hipStream_t>(stream));
 }
 
 int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, int B, int H,

@@ -38,16 +38,21 @@ constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;  // waves per workgroup
 // kFusedSplitV does the same for the fused split (grid z = 2 P, z = 2 part +
 // slice): each slice stores its half of a partition's sums (slice 0 also the
 // (max, sum) pair), a unit's ticket counts the arrivals of both slices, and
-// the last of them merges the whole head dim.
+// the last of them merges the whole head dim.  kPartialsSplitV is kPartials
+// split the same way, for the shapes built only with V split
+// (v_split_only); its partials have the layout of kPartials.
 enum Mode {
     kSingle = 0,
     kPartials = 1,
     kFused = 2,
     kFusedLate = 3,
     kSingleSplitV = 4,
-    kFusedSplitV = 5
+    kFusedSplitV = 5,
+    kPartialsSplitV = 6
 };
-constexpr int v_slices(int mode) { return mode == kSingleSplitV || mode == kFusedSplitV ? 2 : 1; }
+constexpr int v_slices(int mode) {
+    return mode == kSingleSplitV || mode == kFusedSplitV || mode == kPartialsSplitV ? 2 : 1;
+}
 
 // The V-split modes are built for head dims of at least 128 (a half row then still
 // gives each lane whole 8- or 16-byte V loads).
@@ -92,16 +97,31 @@ struct MergeParams {
     int B, H, P, d;
 };
 
-// The (dtype, head dim, group size) combinations with a kernel.  One
-// workgroup keeps the fp32 accumulators of all G heads of its group in
-// registers (G * d / 16 per lane) next to the tiles in flight; the
-// combinations left out would not fit the register file without spilling to
-// scratch memory.
+// The (dtype, head dim, group size) combinations with a kernel: head dims
+// 64, 128 and 256, groups of 1 to 16 query heads per kv head.
 constexpr bool shape_built(int dtype, int d, int G) {
+    (void)dtype;
     if (d != 64 && d != 128 && d != 256) return false;
-    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
-    if (d == 256) return dtype == PA_DTYPE_F32 ? G <= 2 : G <= 8;
-    return true;
+    return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
+}
+
+// The shapes built only in the V-split modes.  One workgroup keeps the fp32
+// accumulators of all G heads of its group in registers (G * DV / 16 per lane,
+// DV the head dim of V it serves) next to the tiles in flight: with d = 256
+// and G = 16 (or G >= 8 for fp32) the whole head dim would spill to scratch
+// memory, half of it fits.  For these the launcher always splits V's head dim
+// over two workgroups.
+constexpr bool v_split_only(int dtype, int d, int G) {
+    return d == 256 && (dtype == PA_DTYPE_F32 ? G >= 8 : G >= 16);
+}
+
+// Whether the kernel of (dtype, d, G) is built in `mode`.  kPartialsSplitV
+// only for the V-split-only shapes (the others use kPartials).
+constexpr bool mode_built(int dtype, int d, int G, int mode) {
+    if (!shape_built(dtype, d, G)) return false;
+    if (mode == kPartialsSplitV) return v_split_only(dtype, d, G);
+    if (v_slices(mode) > 1) return split_v_built(d);
+    return !v_split_only(dtype, d, G);
 }
 
 // Ints between the arrival tickets of two (sequence, kv head) units, so that
@@ -130,7 +150,7 @@ constexpr int kMaxGridY = 65535;
 
 // Launch the decode kernel for element type DT on a (Hkv, nseq, P) grid of
 // kWavesPerGroup-wave workgroups covering sequences p.b0 .. p.b0 + nseq - 1
-// (shape_built(DT, d, G) must hold), or the merge kernel on one wave per
+// (mode_built(DT, d, G, mode) must hold), or the merge kernel on one wave per
 // (b, h).  Return the launch's hipGetLastError().
 template <int DT>
 hipError_t launch_decode(const Params &p, int d, int G, int mode, int nseq,

@@ -997,10 +997,11 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         } else if (direct) {
             const float inv = L > 0.f ? 1.f / L : 0.f;
             store_pair<DT>(p.out, bh * D + vslice * DV + e, o0 * inv, o1 * inv);
-        } else if constexpr (MODE == kPartials) {
-            *reinterpret_cast<float2 *>(p.part_acc + (bh * p.P + part) * D + e) =
+        } else if constexpr (MODE == kPartials || MODE == kPartialsSplitV) {
+            // (with V split, each slice stores its half; slice 0 the (max, sum))
+            *reinterpret_cast<float2 *>(p.part_acc + (bh * p.P + part) * D + vslice * DV + e) =
                 make_float2(o0, o1);
-            if (e == 0) p.part_ml[bh * p.P + part] = make_float2(M, L);
+            if (e == 0 && vslice == 0) p.part_ml[bh * p.P + part] = make_float2(M, L);
         } else {
             // (with V split, each slice stores its half; slice 0 the (max, sum))
             store_pair_coherent(p.part_acc + (bh * p.P + part) * D + vslice * DV + e, o0, o1);
@@ -1129,7 +1130,7 @@ __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
 
 template <int DT, int D, int G, int MODE>
 hipError_t launch_instance(const Params &p, int nseq, hipStream_t stream) {
-    if constexpr (shape_built(DT, D, G)) {
+    if constexpr (mode_built(DT, D, G, MODE)) {
         hipLaunchKernelGGL((pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
                            dim3(p.Hkv, nseq, v_slices(MODE) * p.P),
                            dim3(kWavesPerGroup * kWave), 0, stream, p);
@@ -1162,6 +1163,9 @@ hipError_t dispatch_mode(const Params &p, int G, int mode, int nseq, hipStream_t
             if constexpr (split_v_built(D)) return dispatch_g<DT, D, kFusedSplitV>(p, G, nseq, stream);
             else return hipErrorInvalidValue;
         case kPartials: return dispatch_g<DT, D, kPartials>(p, G, nseq, stream);
+        case kPartialsSplitV:
+            if constexpr (split_v_built(D)) return dispatch_g<DT, D, kPartialsSplitV>(p, G, nseq, stream);
+            else return hipErrorInvalidValue;
         case kFused: return dispatch_g<DT, D, kFused>(p, G, nseq, stream);
         default: return dispatch_g<DT, D, kFusedLate>(p, G, nseq, stream);
     }

@@ -114,14 +114,46 @@ def test_plan(args, expect):
     assert pa.pa_plan(*args) == expect
 
 
+@pytest.mark.parametrize("dtype,G,split_only", [
+    (pa.PA_DTYPE_BF16, 8, False), (pa.PA_DTYPE_BF16, 16, True), (pa.PA_DTYPE_F16, 16, True),
+    (pa.PA_DTYPE_F32, 4, False), (pa.PA_DTYPE_F32, 8, True), (pa.PA_DTYPE_F32, 16, True),
+])
+def test_plan_of_shapes_that_always_split_v(dtype, G, split_only):
+    # d = 256 with the groups whose whole-row accumulators would not fit the
+    # register file: V split whatever the launch's size, and half the
+    # heuristic's partitions while the units are fewer than the CUs
+    for B, Hkv, W, parts in ((1, 8, 1024, 0), (40, 8, 256, 0), (2, 8, 64, 5), (64, 8, 64, 1),
+                             (2, 8, 4, 0)):
+        got = pa.pa_plan(B, Hkv, 256, W, 16, 256, parts, H=G * Hkv, dtype=dtype)
+        ref = pa.pa_plan(B, Hkv, 256, W, 16, 256, parts)      # G = 1: never forced
+        if not split_only:
+            assert got == ref, (B, W, parts)
+            continue
+        assert got[1] == 2, (B, W, parts)
+        if parts == 0 and B * Hkv < 256 and ref[0] > 1:
+            assert got[0] == max(1, ref[0] // 2), (B, W, got, ref)
+        elif parts == 0 and B * Hkv < 256:
+            assert got[0] == 1
+        else:
+            assert got[0] == ref[0], (B, W, parts)
+
+
 def test_plan_rejects_bad_arguments():
     lib = pa.load()
     import ctypes
     P, vs = ctypes.c_int(), ctypes.c_int()
-    assert lib.pa_plan(1, 8, 128, 4, 16, 256, 0, None, ctypes.byref(vs)) == pa.PA_ERR_NULL
-    bad = [((1, 0, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 0, 0), pa.PA_ERR_SHAPE),
-           ((-1, 8, 128, 4, 16, 256, 0), pa.PA_ERR_SHAPE), ((1, 8, 128, 4, 16, 256, -2), pa.PA_ERR_VALUE),
-           ((1, 8, 96, 4, 16, 256, 0), pa.PA_ERR_UNSUPPORTED), ((1, 8, 128, 4, 8, 256, 0), pa.PA_ERR_UNSUPPORTED)]
+    # (B, H, Hkv, d, dtype, max_blocks, block_size, num_cus, num_partitions)
+    assert lib.pa_plan(1, 32, 8, 128, 1, 4, 16, 256, 0, None, ctypes.byref(vs)) == pa.PA_ERR_NULL
+    bad = [((1, 32, 0, 128, 1, 4, 16, 256, 0), pa.PA_ERR_SHAPE),
+           ((1, 32, 8, 128, 1, 4, 16, 0, 0), pa.PA_ERR_SHAPE),
+           ((-1, 32, 8, 128, 1, 4, 16, 256, 0), pa.PA_ERR_SHAPE),
+           ((1, 0, 8, 128, 1, 4, 16, 256, 0), pa.PA_ERR_SHAPE),
+           ((1, 12, 8, 128, 1, 4, 16, 256, 0), pa.PA_ERR_SHAPE),
+           ((1, 32, 8, 128, 7, 4, 16, 256, 0), pa.PA_ERR_DTYPE),
+           ((1, 32, 8, 128, 1, 4, 16, 256, -2), pa.PA_ERR_VALUE),
+           ((1, 32, 8, 96, 1, 4, 16, 256, 0), pa.PA_ERR_UNSUPPORTED),
+           ((1, 32, 8, 128, 1, 4, 8, 256, 0), pa.PA_ERR_UNSUPPORTED),
+           ((1, 256, 8, 128, 1, 4, 16, 256, 0), pa.PA_ERR_UNSUPPORTED)]   # G = 32
     for a, code in bad:
         assert lib.pa_plan(*a, ctypes.byref(P), ctypes.byref(vs)) == code, a
 
@@ -149,8 +181,7 @@ def call(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), pa.PA_ERR_UNSUPPORTED),
     (dict(d=32), pa.PA_ERR_UNSUPPORTED),
-    (dict(d=256, H=128, Hkv=8), pa.PA_ERR_UNSUPPORTED),          # G = 16 at d = 256
-    (dict(d=256, H=32, Hkv=8, dtype=0), pa.PA_ERR_UNSUPPORTED),  # fp32, G = 4 at d = 256
+    (dict(d=256, H=256, Hkv=8), pa.PA_ERR_UNSUPPORTED),          # G = 32
     (dict(Hkv=1 << 20, H=1 << 20), pa.PA_ERR_UNSUPPORTED),      # tile offsets past 2^31
     (dict(B=1 << 26, H=64, Hkv=8), pa.PA_ERR_UNSUPPORTED),      # 2^32 (sequence, head) pairs
     (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
@@ -190,12 +221,11 @@ def test_valid_call_without_device_reports_device_error():
     assert call() == pa.PA_ERR_DEVICE
     for bs in (16, 32, 64, 128, 256):  # every supported block size passes validation
         assert call(bs=bs) == pa.PA_ERR_DEVICE
-    for dtype in (0, 1, 2):
+    for dtype in (0, 1, 2):     # every (dtype, d, G) of the supported set is built
         for d in (64, 128, 256):
             for H in (8, 16, 32, 64, 128):
-                built = d < 256 or H // 8 <= (2 if dtype == 0 else 8)
-                want = pa.PA_ERR_DEVICE if built else pa.PA_ERR_UNSUPPORTED
-                assert call(dtype=dtype, d=d, H=H, Hkv=8) == want, (dtype, d, H)
+                assert call(dtype=dtype, d=d, H=H, Hkv=8) == pa.PA_ERR_DEVICE, (dtype, d, H)
+            assert call(dtype=dtype, d=d, H=256, Hkv=8) == pa.PA_ERR_UNSUPPORTED   # G = 32
 
 
 def test_ex_and_split_half_validation():
@@ -370,7 +400,7 @@ def test_no_vsplit_ablation_plans_no_v_split():
     lib = pa.load_variant("no_vsplit")
     P, vs = ctypes.c_int(0), ctypes.c_int(0)
     for B, W in ((1, 32), (16, 16), (1, 1024), (4, 128)):
-        assert lib.pa_plan(B, 8, 128, W, 16, 256, 0, ctypes.byref(P), ctypes.byref(vs)) == 0
+        assert lib.pa_plan(B, 32, 8, 128, 1, W, 16, 256, 0, ctypes.byref(P), ctypes.byref(vs)) == 0
         assert vs.value == 1
         ref = pa.pa_plan(B, 8, 128, W, 16, 256, 0)
         if ref[1] == 1:

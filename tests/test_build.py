@@ -20,10 +20,13 @@ def test_no_kernel_uses_scratch():
         assert len(n) == len(s) and n, src
         names += n
         scratch += s
-    # built (d, G) pairs: fp32 5 + 5 + 2, bf16 and fp16 5 + 5 + 4; 4 modes each, and
-    # the two V-split modes for d >= 128 (fp32 5 + 2, bf16 and fp16 5 + 4)
+    # (d, G) pairs built in the 4 modes without V split: fp32 5 + 5 + 3, bf16
+    # and fp16 5 + 5 + 4 (d = 256 with larger groups only splits V); the two
+    # V-split modes for every G at d >= 128 (5 + 5 per dtype); and the split
+    # kernel with V split for the shapes that always split it (fp32 G = 8,
+    # 16 and 16-bit G = 16 at d = 256)
     decode = [n for n in names if "pa_decode_kernel" in n]
-    assert len(decode) == (12 + 14 + 14) * 4 + (7 + 9 + 9) * 2
+    assert len(decode) == (13 + 14 + 14) * 4 + (10 + 10 + 10) * 2 + (2 + 1 + 1)
     assert sum("pa_merge_kernel" in n for n in names) == 3
     bad = [n for n, s in zip(names, scratch) if s != 0]
     assert not bad, f"kernels using scratch: {bad}"

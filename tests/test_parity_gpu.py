@@ -461,8 +461,6 @@ def test_rising_scores_move_the_reference_max(gpu, dtype, shape):
     # without the V split), forced splits 3 and 33, the heuristic through
     # pa_decode and pa_decode_ex, and a caller workspace (two kernels).
     lens, H, Hkv, d, holes = shape
-    if not pa_shape_built(dtype, d, H // Hkv):
-        pytest.skip("shape not built")
     case = staircase_case(dtype, lens, H, Hkv, d, seed=sum(lens) + H + d, holes=holes)
     margin = staircase_margin(case)
     assert margin > 8.0, f"inputs do not force the rescale (margin {margin:.2f})"
@@ -478,14 +476,6 @@ def test_rising_scores_move_the_reference_max(gpu, dtype, shape):
             workspace = (torch.empty(nbytes, dtype=torch.uint8, device=gpu), nbytes)
         out = run_gpu(case, gpu, num_partitions=parts, workspace=workspace)
         assert_close(to_f64(out), ref, dtype, f"staircase {label}")
-
-
-def pa_shape_built(dtype, d, G):
-    """The (dtype, head dim, group size) combinations the library builds (the
-    header's supported set)."""
-    if d == 256:
-        return G <= 2 if dtype == "f32" else G <= 8
-    return True
 
 
 def test_graph_replay_matches_eager(gpu):
@@ -699,13 +689,6 @@ def test_script_default_sweep(gpu, dtype, B, seq):
     assert_close(to_f64(out), oracle.decode_case(case), dtype, f"sweep B={B} seq={seq}")
 
 
-def built(dtype, d, G):
-    # the (dtype, head dim, group size) combinations the library has kernels for
-    if d == 256:
-        return G <= (2 if dtype == "f32" else 8)
-    return True
-
-
 HEAD_DIM_CASES = [
     # B, lens, H, Hkv, bs, holes
     (3, [1, 100, 700], 32, 8, 16, [(2, 5)]),
@@ -722,8 +705,6 @@ HEAD_DIM_CASES = [
 @pytest.mark.parametrize("parts", [0, 1, 5])
 def test_head_dims(gpu, dtype, d, shape, parts):
     B, lens, H, Hkv, bs, holes = shape
-    if not built(dtype, d, H // Hkv):
-        pytest.skip(f"no kernel for {dtype} d={d} G={H // Hkv}: returns PA_ERR_UNSUPPORTED")
     max_blocks = max(math.ceil(n / bs) for n in lens) + 1
     need = sum(math.ceil(n / bs) for n in lens)
     case = pi.make_case(B, lens, H, Hkv, d, bs, dtype=dtype, seed=d + bs + sum(lens),
@@ -739,13 +720,58 @@ def test_head_dims(gpu, dtype, d, shape, parts):
     assert torch.equal(a, b)
 
 
-def test_unbuilt_shape_is_rejected(gpu):
-    case = pi.make_case(1, 40, 128, 8, 256, 16, dtype="bf16", seed=1)
+def test_unsupported_group_is_rejected(gpu):
+    case = pi.make_case(1, 40, 256, 8, 128, 16, dtype="bf16", seed=1)   # G = 32
     d = DeviceCase(case, gpu)
     out = torch.empty_like(d.q)
     with pytest.raises(pa.PaError) as e:
         pa.pa_decode(out, *d.args(), None)
     assert e.value.code == pa.PA_ERR_UNSUPPORTED
+
+
+# d = 256 with the groups whose whole-row accumulators would not fit a
+# workgroup's registers: the launcher always splits V's head dim over two
+# workgroups (single pass, fused split, and the split kernel of a caller
+# workspace or of pa_decode_partials, whose partials the merge kernel reads).
+SPLIT_ONLY_CASES = [
+    # (dtype, B, lens, H, Hkv, holes)
+    ("bf16", 3, [1500, 37, 700], 32, 2, [(0, 20)]),
+    ("f16", 2, [3000, 410], 64, 4, []),
+    ("f32", 3, [900, 5, 260], 32, 4, [(2, 3)]),
+    ("f32", 2, [2000, 1100], 16, 1, []),
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_ONLY_CASES, ids=lambda s: f"{s[0]}_G{s[3] // s[4]}")
+def test_shapes_that_always_split_v(gpu, shape):
+    dtype, B, lens, H, Hkv, holes = shape
+    G = H // Hkv
+    case = pi.make_case(B, lens, H, Hkv, 256, 16, dtype=dtype, seed=sum(lens) + G, holes=holes)
+    ref = oracle.decode_case(case)
+    cus = pa.pa_device_num_cus(0)
+    code = pa.dtype_code({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype])
+    for parts in (0, 1, 3, 33):
+        P, vs = pa.pa_plan(B, Hkv, 256, case.max_blocks, 16, cus, parts, H=H, dtype=code)
+        assert vs == 2
+        say(f"always-split {dtype} G={G} lens {lens} P={parts} (plan {P} x {vs})")
+        out = run_gpu(case, gpu, num_partitions=parts)
+        assert_close(to_f64(out), ref, dtype, f"{dtype} G={G} P={parts}")
+    # caller workspace: the split kernel with V split, then the merge kernel
+    d = DeviceCase(case, gpu)
+    nbytes = pa.pa_workspace_bytes(B, H, 256, 5)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu)
+    say(f"always-split {dtype} G={G}: caller workspace, split halves, no allocation")
+    out = run_gpu(case, gpu, num_partitions=5, workspace=(ws, nbytes))
+    assert_close(to_f64(out), ref, dtype, f"{dtype} G={G} caller workspace")
+    halves = torch.empty_like(d.q)
+    pa.pa_decode_partials(*d.args(), 5, 0, ws, nbytes)
+    pa.pa_merge_partials(halves, ws, nbytes, B, H, 256, 5, d.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(halves, out)
+    na = torch.empty_like(d.q)
+    pa.pa_decode_noalloc(na, *d.args(), None)
+    torch.cuda.synchronize()
+    assert torch.equal(na, run_gpu(case, gpu))
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
@@ -953,8 +979,6 @@ def random_case(seed):
     dtype = ["f32", "bf16", "f16"][rng.integers(3)]
     d = [64, 128, 256][rng.integers(3)]
     G = [1, 2, 4, 8, 16][rng.integers(5)]
-    if not built(dtype, d, G):
-        G = 2
     Hkv = int(rng.choice([1, 2, 4, 8]))
     bs = int(2 ** rng.integers(4, 9))
     B = int(rng.integers(1, 7))
@@ -1102,8 +1126,6 @@ SHARED_MERGE_CASES = [
 @pytest.mark.parametrize("shape", SHARED_MERGE_CASES, ids=lambda s: f"H{s[2]}_Hkv{s[3]}_d{s[4]}")
 def test_shared_merge(gpu, dtype, shape):
     B, ctx, H, Hkv, d = shape
-    if not pa_shape_built(dtype, d, H // Hkv):
-        pytest.skip("shape not built")
     case = pi.make_case(B, ctx - 37, H, Hkv, d, 16, dtype=dtype, seed=ctx + H + d)
     cus = pa.pa_device_num_cus(0)
     P, vs = pa.pa_plan(B, Hkv, d, case.max_blocks, 16, cus)
