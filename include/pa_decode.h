@@ -123,9 +123,10 @@ enum {
  * workgroup of a non-empty partition writes its (max, sum, weighted values) to
  * a library-owned workspace and takes an atomic ticket; the last workgroup of
  * each (sequence, kv head) merges those partials and writes out (shared with
- * the 1 or 3 arrivals before it, each taking one slice of the head dim, when
- * the unit's partials are at least 48 KiB and the launch's workgroups fit the
- * device at once, at most one per compute unit).  When the
+ * the arrivals before it, each taking one slice of the head dim of about
+ * 8 KiB of partials, 2 to 16 slices in all, when the unit's partials are at
+ * least 48 KiB and the launch's workgroups fit the device at once, at most
+ * one per compute unit).  When the
  * B * Hkv * P workgroups fill at most a quarter of the compute units (and
  * d >= 128), each partition is again served by two workgroups, one per half
  * of V's head dim, and the ticket counts both.  The shapes that always split V

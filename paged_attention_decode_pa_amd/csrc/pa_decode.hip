@@ -368,21 +368,33 @@ Plan make_plan(int B, int Hkv, int d, int max_blocks, int block_size, int cus,
     return plan;
 }
 
-// Workgroups that share each fused merge: kMergeWays when a unit's partials
-// are at least kSharedMergeBytes and every workgroup of the launch can be
-// resident at once (at most one per compute unit), since the waiting mergers
-// then wait only for running workgroups; else the last arrival merges alone.
-// A waiting merger learns that the last partition is in about a microsecond
-// after the last arrival does, so sharing pays only when reading the whole
-// unit's partials through one CU takes longer than that (measured, 4 ways:
-// -0.3 us with 64 KiB per unit, +0.4 to +0.7 us with 16 KiB or less).
+// Workgroups that share each fused merge.  Only when a unit's partials are at
+// least kSharedMergeBytes and every workgroup of the launch can be resident at
+// once (at most one per compute unit), since the waiting mergers then wait
+// only for running workgroups; else the last arrival merges alone.  A waiting
+// merger learns that the last partition is in about a microsecond after the
+// last arrival does, so sharing pays only when reading the whole unit's
+// partials through one CU takes longer than that (measured: -0.3 us with 64
+// KiB per unit, +0.4 to +0.7 us with 16 KiB or less).  Then the partials are
+// cut into slices of about kMergeBytesPerWay each (a power of two of them, at
+// most kMergeWays): one CU reads them at a rate set by its loads in flight,
+// so smaller slices finish sooner (measured against 4 fixed ways: 8 ways -0.1
+// to -0.2 us at 64-94 KiB per unit, -0.8 us at 512 KiB).
 constexpr long long kSharedMergeBytes = 48 << 10;
+#ifndef PA_MERGE_BYTES_PER_WAY
+#define PA_MERGE_BYTES_PER_WAY (8 << 10)
+#endif
+constexpr long long kMergeBytesPerWay = PA_MERGE_BYTES_PER_WAY;
 int merge_ways(int mode, int B, int Hkv, int G, int d, int P, int cus) {
     if (mode != kFused && mode != kFusedSplitV) return 1;
-    if ((long long)P * G * d * 4 < kSharedMergeBytes) return 1;
+    const long long bytes = (long long)P * G * d * 4;
+    if (bytes < kSharedMergeBytes) return 1;
     const long long per_launch =
         (long long)(B < kMaxGridY ? B : kMaxGridY) * Hkv * P * v_slices(mode);
-    return per_launch <= cus ? kMergeWays : 1;
+    if (per_launch > cus) return 1;
+    int ways = 2;
+    while (ways < kMergeWays && bytes > ways * kMergeBytesPerWay) ways *= 2;
+    return ways;
 }
 
 int choose_partitions(int B, int Hkv, int max_blocks, int block_size, int num_cus) {

@@ -134,10 +134,10 @@ constexpr bool mode_built(int dtype, int d, int G, int mode) {
 #endif
 constexpr int kTicketStride = PA_TICKET_STRIDE;
 
-// Workgroups that share a fused merge (p.merge_ways) when a launch's
-// workgroups can all be resident at once (at most one per compute unit).
+// At most this many workgroups share a fused merge (p.merge_ways; the kernel
+// builds the merge for 1, 2, 4, 8 and 16 slices of the head dim).
 #ifndef PA_MERGE_WAYS
-#define PA_MERGE_WAYS 4
+#define PA_MERGE_WAYS 16
 #endif
 constexpr int kMergeWays = PA_MERGE_WAYS;
 // Rounds a merger waits for the generation of its ticket to move on before it

@@ -604,7 +604,8 @@ constexpr int kCoherent = 16;
 template <int DT, int D, int G, int NW, int WAYS = 1>
 constexpr int merge_split() {
     constexpr int kThreads = NW * kWave, kItems = G * D / (4 * WAYS);
-    return kItems >= kThreads ? 1 : kThreads / kItems;
+    // (at most a wave: with few items the waves past kItems * S have none)
+    return kItems >= kThreads ? 1 : (kThreads / kItems > kWave ? kWave : kThreads / kItems);
 }
 
 template <int DT, int D, int G, int NW, int CH, int WAYS>
@@ -615,8 +616,9 @@ __device__ __forceinline__ void merge_group_chunked(const Params &p, int b, int 
     constexpr int kItems = G * kQuads;
     constexpr int S = merge_split<DT, D, G, NW, WAYS>();
     static_assert(S <= kWave, "the butterfly stays inside a wave");
-    static_assert(kItems % kThreads == 0 || kItems * S == kThreads,
-                  "every thread must take part in the butterfly");
+    static_assert(kItems >= 1, "a slice holds at least one quad of the head dim");
+    static_assert(kItems % kThreads == 0 || (kItems * S) % kWave == 0,
+                  "every thread of a wave with items takes part in the butterfly");
     const long long bh0 = (long long)b * p.H + kvh * G;
     const __amdgpu_buffer_rsrc_t rml =
         buffer_rsrc(reinterpret_cast<const char *>(p.part_ml + bh0 * p.P), G * p.P * 8);
@@ -685,7 +687,9 @@ __device__ __forceinline__ void merge_group_ways(const Params &p, int b, int kvh
 template <int DT, int D, int G, int NW>
 __device__ __forceinline__ void merge_group(const Params &p, int b, int kvh, int busy, int ways,
                                             int slice, bool poisoned) {
-    if (ways == 4) merge_group_ways<DT, D, G, NW, 4>(p, b, kvh, busy, slice, poisoned);
+    if (ways == 16) merge_group_ways<DT, D, G, NW, 16>(p, b, kvh, busy, slice, poisoned);
+    else if (ways == 8) merge_group_ways<DT, D, G, NW, 8>(p, b, kvh, busy, slice, poisoned);
+    else if (ways == 4) merge_group_ways<DT, D, G, NW, 4>(p, b, kvh, busy, slice, poisoned);
     else if (ways == 2) merge_group_ways<DT, D, G, NW, 2>(p, b, kvh, busy, slice, poisoned);
     else merge_group_ways<DT, D, G, NW, 1>(p, b, kvh, busy, 0, poisoned);
 }

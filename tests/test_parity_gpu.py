@@ -1113,8 +1113,9 @@ def test_uniform_lengths_hint(gpu, lens):
 SHARED_MERGE_CASES = [
     # (B, ctx, H, Hkv, d): a fused split whose (sequence, kv head) units hold
     # at least 48 KiB of partial sums, with at most one workgroup per CU, so
-    # that the last 4 arrivals of each unit share its merge, one quarter of
-    # the head dim each (G = 4, 16, 1 and 4; head dims 128, 128, 256, 64)
+    # that the last arrivals of each unit share its merge, one slice of the
+    # head dim each (8 or 16 of them here; G = 4, 16, 1 and 4; head dims 128,
+    # 128, 256, 64)
     (1, 16384, 32, 8, 128),
     (1, 8192, 16, 1, 128),
     (1, 12000, 4, 4, 256),
@@ -1138,9 +1139,9 @@ def test_shared_merge(gpu, dtype, shape):
 
 
 # Calls on one stream whose fused merges take every path through the library's
-# buffers in turn, each with a layout of its own: a merge shared by the last 4
+# buffers in turn, each with a layout of its own: a merge shared by the last 8
 # arrivals (one long sequence), the last arrival alone (units of 16 KiB of
-# partials), shared by 4 and by 2 in one launch (a ragged batch whose short
+# partials), shared by 8 and by 2 in one launch (a ragged batch whose short
 # sequence has only 2 or 3 partitions), with V split, and with more
 # workgroups than compute units.  Each call must leave its tickets at zero
 # whatever the next call's layout, and no call may take another's partial
