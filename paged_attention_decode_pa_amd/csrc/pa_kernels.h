@@ -45,11 +45,12 @@
 //   LDS, always with the rescale-and-sum rule
 //   (M = max m, L = sum l * 2^(m - M), O = sum acc * 2^(m - M)).  A single
 //   pass writes O / L (in kSingleSplitV two workgroups per unit each do so for
-//   one half of the head dim of V; kFusedSplitV splits V the same way in the
-//   fused split).  With partitions, each workgroup writes (M, L, O) to
-//   the workspace; then either a separate merge kernel combines them, or (fused
-//   mode) the last workgroup of each (b, kvh) to finish -- found with an atomic
-//   ticket -- combines them with the same rule and writes out.
+//   one half of the head dim of V; kFusedSplitV and kPartialsSplitV split V
+//   the same way in the fused split and the split kernel).  With partitions,
+//   each workgroup writes (M, L, O) to the workspace; then either a separate
+//   merge kernel combines them, or (fused mode) the last workgroups of each
+//   (b, kvh) to finish -- found with an atomic ticket -- combine them with the
+//   same rule and write out, each one slice of the head dim.
 //
 // Build-time settings (macros).  libpa_decode.so is built with the defaults;
 // the other values exist only to measure the alternatives the defaults were
@@ -1026,11 +1027,12 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
         // is 64 bits, an arrival count (low half) and a generation (high
         // half).  Of the n = VS * busy workgroups, the last to arrive (count
         // n - 1) resets the count and moves the generation on with one
-        // atomic add, and merges; with p.merge_ways = K > 1 the K - 1 before
-        // it (counts n - K .. n - 2) merge too, each its own slice of the
-        // head dim, once they see the generation move on (a bounded wait on
-        // the ticket's line).  K > 1 only when every workgroup of the launch
-        // can be resident at once, so the ones they wait for are running.
+        // atomic add, and merges; with K > 1 (K the largest power of two up
+        // to p.merge_ways that n fills) the K - 1 before it (counts n - K ..
+        // n - 2) merge too, each its own slice of the head dim, once they see
+        // the generation move on (a bounded wait on the ticket's line).
+        // p.merge_ways > 1 only when every workgroup of the launch can be
+        // resident at once, so the ones they wait for are running.
         //
         // Ordering (PA_ORDERED_TICKET = 0, the library): the partial sums are
         // agent-scope atomic stores, which on this part write through to the
