@@ -4,8 +4,9 @@ library's fixed device array, so its output must equal pa_decode's bit for
 bit (same kernels, same partition count, same reduction order), and match the
 oracle at the stated tolerance.  Two calls in a row, the second smaller, so
 the array is reused with the previous call's contents in it; a covering batch
-(late-query fused split) and a single pass; and a split too large for the
-array is refused before anything is launched."""
+(late-query fused split) and a single pass; a split too large for the
+array is refused before anything is launched; and the call captured in a HIP
+graph and replayed, with other calls on the array in between."""
 import numpy as np
 import pytest
 import torch
@@ -90,3 +91,37 @@ def test_noalloc_refuses_a_split_beyond_its_array(gpu):
     assert e.value.code == pa.PA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())   # nothing was launched
+
+
+@pytest.mark.parametrize("B,lens", [(1, 16384), (4, 2048), (40, [2200, 300] * 20)])
+def test_noalloc_replayed_from_a_captured_graph(gpu, B, lens):
+    # the callers it is for capture it: the call records its kernels (and
+    # nothing that allocates) on a fresh stream, and every replay, with other
+    # calls on the device array in between, equals pa_decode bit for bit
+    case = pi.make_case(B, lens, 32, 8, 128, 16, dtype="bf16", seed=700 + B)
+    check_host_preconditions(case)
+    d = DeviceCase(case, gpu)
+    ref = torch.empty_like(d.q)
+    pa.pa_decode(ref, *d.args(), None)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    out = torch.empty_like(d.q)
+    say(f"noalloc under graph capture: B={B}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        pa.pa_decode_noalloc(out, *d.args(), s)
+        g.capture_end()
+    torch.cuda.synchronize()
+    other = pi.make_case(1, 3000, 32, 8, 128, 16, dtype="bf16", seed=701)
+    od = DeviceCase(other, gpu)
+    oo = torch.empty_like(od.q)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        pa.pa_decode_noalloc(oo, *od.args(), None)   # the array in between
+        torch.cuda.synchronize()
+    assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"noalloc graph B={B}")
