@@ -678,6 +678,15 @@ __device__ __forceinline__ void merge_group_ways(const Params &p, int b, int kvh
                                                  int slice, bool poisoned) {
     constexpr int S = merge_split<DT, D, G, NW, WAYS>();
     const int share = (busy + S - 1) / S;  // partitions per thread
+    if constexpr (WAYS >= 4) {
+        // (a wide merge's threads share few partitions each: chunks of up to 4,
+        // looped over for more, keep the code the kernel carries small -- each
+        // XCD fetches its own copy of it every launch)
+        if (share <= 1) merge_group_chunked<DT, D, G, NW, 1, WAYS>(p, b, kvh, busy, slice, poisoned);
+        else if (share <= 2) merge_group_chunked<DT, D, G, NW, 2, WAYS>(p, b, kvh, busy, slice, poisoned);
+        else merge_group_chunked<DT, D, G, NW, 4, WAYS>(p, b, kvh, busy, slice, poisoned);
+        return;
+    }
     if (share <= 1) merge_group_chunked<DT, D, G, NW, 1, WAYS>(p, b, kvh, busy, slice, poisoned);
     else if (share <= 2) merge_group_chunked<DT, D, G, NW, 2, WAYS>(p, b, kvh, busy, slice, poisoned);
     else if (share <= 4) merge_group_chunked<DT, D, G, NW, 4, WAYS>(p, b, kvh, busy, slice, poisoned);
