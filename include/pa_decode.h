@@ -52,7 +52,9 @@
  *     the HIP runtime, and leave the HIP context unusable.
  *   - q, k_cache, v_cache, out and workspace must be 16-byte aligned;
  *     block_tables and context_lens 4-byte aligned.  out must not overlap q,
- *     k_cache or v_cache.
+ *     k_cache or v_cache, and a caller workspace must not overlap out or q
+ *     (PA_ERR_ALIAS; the library sees no cache sizes, so it checks the
+ *     caches only against out's start).
  *   - The caller owns every buffer.  The library keeps no pointer past the
  *     call, except the workspace it allocates itself (see pa_decode).
  *   - B == 0 is a no-op that returns PA_OK.
@@ -88,7 +90,7 @@ enum {
                              /* would have to allocate one during graph capture */
     PA_ERR_HIP = -7,         /* a HIP runtime call or a launch failed             */
     PA_ERR_DEVICE = -8,      /* no current HIP device                             */
-    PA_ERR_ALIAS = -9,       /* out overlaps an input                             */
+    PA_ERR_ALIAS = -9,       /* out, or a workspace, overlaps an input            */
     PA_ERR_VALUE = -10       /* scale not finite, or a negative count             */
 };
 

@@ -262,7 +262,9 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, out=None, 
     ws_bytes = 0
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
-    pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d, block_size,
-                 max_blocks, float(scale), dtype_code(q.dtype), stream, num_partitions,
-                 num_pool_blocks, workspace, ws_bytes)
+    # (the library launches on the current device and sizes its buffers for it)
+    with torch.cuda.device(q.device):
+        pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
+                     block_size, max_blocks, float(scale), dtype_code(q.dtype), stream,
+                     num_partitions, num_pool_blocks, workspace, ws_bytes)
     return out

@@ -126,6 +126,14 @@ int validate(void *out, const void *q, const void *k_cache, const void *v_cache,
     return PA_OK;
 }
 
+// Whether a caller workspace of `bytes` bytes overlaps out (if given) or q,
+// each B * H * d elements.
+bool workspace_overlaps(const void *ws, size_t bytes, const void *out, const void *q, int B,
+                        int H, int d, int esize) {
+    const size_t qbytes = (size_t)B * H * d * esize;
+    return (out && overlaps(ws, bytes, out, qbytes)) || overlaps(ws, bytes, q, qbytes);
+}
+
 std::mutex g_mutex;
 std::map<int, int> g_cus;  // device -> CU count
 
@@ -494,7 +502,7 @@ const char *pa_strerror(int code) {
                    "scratch";
         case PA_ERR_HIP: return "HIP runtime call or kernel launch failed";
         case PA_ERR_DEVICE: return "no usable HIP device";
-        case PA_ERR_ALIAS: return "out overlaps an input";
+        case PA_ERR_ALIAS: return "out or a caller workspace overlaps q or another buffer";
         case PA_ERR_VALUE: return "scale not finite or a negative count";
         default: return "unknown error code";
     }
@@ -512,6 +520,11 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     if (num_partitions < PA_PARTITIONS_UNIFORM || num_pool_blocks < 0) return PA_ERR_VALUE;
     if (workspace && !aligned(workspace, 16)) return PA_ERR_ALIGN;
     if (B == 0) return PA_OK;
+    // the merge reads the partials while it writes out, and the split reads q
+    // while it writes the partials
+    if (workspace && workspace_bytes > 0 &&
+        workspace_overlaps(workspace, workspace_bytes, out, q, B, H, d, v.esize))
+        return PA_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int dev = 0;
     if ((rc = current_device(&dev)) != PA_OK) return rc;
@@ -622,6 +635,8 @@ int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
     if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
     const int P = num_partitions;
     if (workspace_bytes < workspace_layout(B, H, P, d).total) return PA_ERR_WORKSPACE;
+    if (workspace_overlaps(workspace, workspace_bytes, nullptr, q, B, H, d, v.esize))
+        return PA_ERR_ALIAS;
     Params p = make_params(q, k_cache, v_cache, block_tables, context_lens, B, H, Hkv, d,
                            max_blocks, block_size, scale, v.esize, num_pool_blocks, P);
     attach_workspace(p, workspace, d);

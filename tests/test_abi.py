@@ -242,6 +242,14 @@ def test_ex_and_split_half_validation():
                                   8, 128, 16, 64, 0.088, 1, -1, 0, 0x700000, 1 << 20,
                                   None) == pa.PA_ERR_VALUE
     assert lib.pa_decode_ex(*args, 4, 0, 0x700004, 1 << 20) == pa.PA_ERR_ALIGN
+    # a caller workspace overlapping out or q is refused before any device call
+    # (out and q hold 1 * 32 * 128 bf16 = 8 KiB each)
+    assert lib.pa_decode_ex(*args, 4, 0, FAKE["out"] + 4096, 1 << 20) == pa.PA_ERR_ALIAS
+    assert lib.pa_decode_ex(*args, 4, 0, FAKE["q"] - 4096, 8192) == pa.PA_ERR_ALIAS
+    assert lib.pa_decode_ex(*args, 0, 0, FAKE["out"], 256) == pa.PA_ERR_ALIAS
+    if not torch.cuda.is_available():   # touching neither passes on to the device
+        assert lib.pa_decode_ex(*args, 4, 0, FAKE["q"] - 4096, 4096) == pa.PA_ERR_DEVICE
+        assert lib.pa_decode_ex(*args, 4, 0, FAKE["q"] + 8192, 4096) == pa.PA_ERR_DEVICE
     part = [FAKE["q"], FAKE["k"], FAKE["v"], FAKE["t"], FAKE["n"], 1, 32, 8, 128, 16, 64, 0.088,
             1]
     assert lib.pa_decode_partials(*part, 0, 0, 0x700000, 1 << 20, None) == pa.PA_ERR_VALUE
@@ -250,6 +258,7 @@ def test_ex_and_split_half_validation():
     assert lib.pa_decode_partials(*part, 4, 0, 0x700000, need - 1, None) == pa.PA_ERR_WORKSPACE
     assert lib.pa_decode_partials(*part, 5000, 0, 0x700000, 1 << 30, None) == \
         pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_partials(*part, 4, 0, FAKE["q"] - 64, need, None) == pa.PA_ERR_ALIAS
     assert lib.pa_merge_partials(FAKE["out"], None, need, 1, 32, 128, 4, 1, None) == \
         pa.PA_ERR_WORKSPACE
     assert lib.pa_merge_partials(FAKE["out"], 0x700000, need - 1, 1, 32, 128, 4, 1, None) == \

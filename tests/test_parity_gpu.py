@@ -203,6 +203,60 @@ def test_pool_guard_skips_out_of_range_ids(gpu):
     assert_close(to_f64(out), oracle.decode_case(expect_case), "bf16", "pool guard")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pool_beyond_4_gib(gpu, dtype):
+    # block offsets past 2^31 and 2^32 bytes: the case's blocks are placed in
+    # a device pool of just over 4 GiB per cache, at its start, around the
+    # 2 GiB mark and at its end, every other block NaN.  The kernels walk the
+    # tokens in logical order, so the result is the same bits as on the
+    # case's own compact pool.
+    case = pi.make_case(2, [700, 333], 32, 8, 128, 16, dtype=dtype, seed=23, holes=[(0, 9)])
+    elem = 4 if dtype == "f32" else 2
+    blk_bytes = case.block_size * case.num_kv_heads * case.head_dim * elem
+    big = (1 << 32) // blk_bytes + 64
+    assert big * blk_bytes > 1 << 32
+    mid = (1 << 31) // blk_bytes
+    rng = np.random.default_rng(29)
+    spots = np.concatenate([np.arange(0, 128), np.arange(mid - 64, mid + 64),
+                            np.arange(big - 128, big)])
+    ids = rng.choice(spots, size=case.num_pool_blocks, replace=False)
+    t = case.block_tables
+    far_table = np.where(t >= 0, ids[np.maximum(t, 0)], -1).astype(np.int32)
+    assert (far_table.astype(np.int64) * blk_bytes >= 1 << 32).any()
+    ref = oracle.decode_case(case)
+    small = DeviceCase(case, gpu)
+    tdt = small.k.dtype
+    shape = (big,) + tuple(small.k.shape[1:])
+    kb = torch.full(shape, float("nan"), dtype=tdt, device=gpu)
+    vb = torch.full(shape, float("nan"), dtype=tdt, device=gpu)
+    where = torch.from_numpy(ids.astype(np.int64)).to(gpu)
+    kb[where] = small.k
+    vb[where] = small.v
+    table = torch.from_numpy(far_table).to(gpu)
+    c = case
+    try:
+        for parts, guard in ((None, 0), (0, big), (1, big), (7, 0)):
+            say(f"pool of {big} blocks ({dtype}, {big * blk_bytes} bytes per cache), P={parts}")
+            want = torch.empty_like(small.q)
+            got = torch.empty_like(small.q)
+            if parts is None:
+                pa.pa_decode(want, *small.args(), None)
+                pa.pa_decode(got, small.q, kb, vb, table, small.lens, c.batch, c.num_heads,
+                             c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks,
+                             float(c.scale), small.dtype, None)
+            else:
+                pa.pa_decode_ex(want, *small.args(), None, parts, 0, None, 0)
+                pa.pa_decode_ex(got, small.q, kb, vb, table, small.lens, c.batch, c.num_heads,
+                                c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks,
+                                float(c.scale), small.dtype, None, parts, guard, None, 0)
+            torch.cuda.synchronize()
+            assert_close(to_f64(got), ref, dtype, f"far pool P={parts}")
+            assert torch.equal(got, want), f"far pool P={parts}: bits differ from compact pool"
+    finally:
+        del kb, vb
+        torch.cuda.empty_cache()
+
+
 def test_non_default_stream(gpu):
     case = pi.make_config_case(3)
     s = torch.cuda.Stream()
