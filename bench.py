@@ -711,6 +711,10 @@ def timeline(case, dev, steps, warmup, use_graph, parts):
                entry=q(us(st[:, 0])), loop_end=q(loop_end),
                per_xcd_loop_end_median={int(x): round(float(pct(loop_end[xcc == x], 0.5)), 2)
                                         for x in sorted(set(xcc.tolist()))},
+               # kv head fastest in the grid: workgroup i serves kv head i mod Hkv
+               per_kv_head_loop_end_median={
+                   h: round(float(pct(loop_end[np.arange(nwg) % c.num_kv_heads == h], 0.5)), 2)
+                   for h in range(c.num_kv_heads)},
                # workgroups dealt to the 8 XCDs round-robin by linear id, from an
                # XCD that need not be 0: the share of workgroups on XCD
                # (linear id + the most common offset) mod 8, and that offset
