@@ -90,6 +90,10 @@ def parse():
     ap.add_argument("--timeline", action="store_true",
                     help="instead of the bench line, the per-workgroup timeline of the timed "
                          "workload's last graph-replayed step (libpa_decode_timeline.so)")
+    ap.add_argument("--timeline-runs", type=int, default=1, metavar="N",
+                    help="with --timeline: measure N times in one process (the XCD that runs "
+                         "each kv head's units moves from one measurement to the next) and add "
+                         "every run's per-kv-head and per-XCD medians")
     ap.add_argument("--leg", default=None, metavar="WORKLOAD:PARTITIONS",
                     help=argparse.SUPPRESS)   # one per-config leg, run as a child process
     ap.add_argument("--sweep", nargs="?", const="design-note", default=None,
@@ -875,8 +879,14 @@ def main():
         headline = pi.make_config_case(args.workload)
 
     if args.timeline:
-        print(json.dumps(timeline(headline, dev, min(args.steps, 200), args.warmup, use_graph,
-                                  args.partitions)), flush=True)
+        runs = [timeline(headline, dev, min(args.steps, 200), args.warmup, use_graph,
+                         args.partitions) for _ in range(max(1, args.timeline_runs))]
+        out = runs[0]
+        if len(runs) > 1:
+            keep = ("xcd_offset", "per_kv_head_loop_end_median", "per_xcd_loop_end_median",
+                    "step_end")
+            out["runs"] = [{k: r[k] for k in keep} for r in runs]
+        print(json.dumps(out), flush=True)
         return
 
     w, t_step, t_min, err = measure(headline, dev, args.steps, args.warmup, use_graph,
