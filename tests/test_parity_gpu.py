@@ -158,6 +158,102 @@ def test_repeatable_bitwise(gpu):
     assert torch.equal(a, b)
 
 
+def scaling_cases(dtype):
+    """A ragged case with a hole, and the full-size workloads of the dtype."""
+    ragged = pi.make_case(3, [700, 1, 260], 32, 8, 128, 16, dtype=dtype, seed=31,
+                          holes=[(0, 7)])
+    return [ragged] + ([pi.make_config_case(c) for c in (4, 5)] if dtype == "bf16"
+                       else [pi.make_config_case(1)])
+
+
+def decode_paths(d, q, v, scale, gpu):
+    """Outputs of one inputs set on the heuristic fused path, the single pass,
+    a forced split of 5 through the library's buffers and through a caller
+    workspace (split kernel, then the merge kernel)."""
+    c = d.case
+    args = lambda: (q, d.k, v, d.table, d.lens, c.batch, c.num_heads, c.num_kv_heads,
+                    c.head_dim, c.block_size, c.max_blocks, scale, d.dtype, None)
+    ws_bytes = pa.pa_workspace_bytes(c.batch, c.num_heads, c.head_dim, 5)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=gpu)
+    outs = []
+    for parts, workspace in ((None, None), (1, None), (5, None), (5, ws)):
+        out = torch.empty_like(q)
+        if parts is None:
+            pa.pa_decode(out, *args())
+        else:
+            pa.pa_decode_ex(out, *args(), parts, 0, workspace,
+                            ws_bytes if workspace is not None else 0)
+        outs.append(out)
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [60, -60])
+def test_scaling_v_by_a_power_of_two_scales_out_exactly(gpu, dtype, k):
+    # V enters only through products with the weights, sums, rescales by
+    # factors of the scores, the merge and the division by the normaliser,
+    # and the output's rounding: all commute exactly with a power-of-two
+    # scale while nothing overflows or turns subnormal.  So out(2^k V) is
+    # 2^k out(V) bit for bit on every path, at any size.
+    for case in scaling_cases(dtype):
+        d = DeviceCase(case, gpu)
+        say(f"V scaled by 2^{k}: {case.name or 'ragged'} ({dtype})")
+        v2 = (d.v.double() * 2.0 ** k).to(d.v.dtype)
+        assert torch.equal((v2.double() * 2.0 ** -k).to(d.v.dtype), d.v)  # the scaling is exact
+        base = decode_paths(d, d.q, d.v, float(case.scale), gpu)
+        scaled = decode_paths(d, d.q, v2, float(case.scale), gpu)
+        for i, (a, b) in enumerate(zip(base, scaled)):
+            assert torch.isfinite(a).all()
+            want = (a.double() * 2.0 ** k).to(a.dtype)
+            assert torch.equal(b, want), f"path {i}: out(2^{k} V) != 2^{k} out(V)"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [20, -20])
+def test_scale_moved_into_the_query_gives_the_same_bits(gpu, dtype, k):
+    # The score is the fp32 dot product q.K (exact products, fp32 sums) times
+    # fp32(scale * log2 e).  With q scaled by 2^k and the scale by 2^-k, the
+    # dot product and that factor scale exactly by 2^k and 2^-k, so every
+    # score, and so the output, keeps its bits.  A scale folded into a
+    # rounded copy of q, or applied twice, breaks this.
+    for case in scaling_cases(dtype):
+        d = DeviceCase(case, gpu)
+        say(f"q scaled by 2^{k}, scale by 2^{-k}: {case.name or 'ragged'} ({dtype})")
+        q2 = (d.q.double() * 2.0 ** k).to(d.q.dtype)
+        assert torch.equal((q2.double() * 2.0 ** -k).to(d.q.dtype), d.q)
+        s = float(case.scale)
+        s2 = float(np.float32(s) * np.float32(2.0 ** -k))
+        assert s2 * 2.0 ** k == s
+        base = decode_paths(d, d.q, d.v, s, gpu)
+        moved = decode_paths(d, q2, d.v, s2, gpu)
+        for i, (a, b) in enumerate(zip(base, moved)):
+            assert torch.isfinite(a).all()
+            assert torch.equal(a, b), f"path {i}: bits changed with the scale moved into q"
+
+
+def test_batch_order_permutes_rows_bitwise(gpu):
+    # every (sequence, kv head) unit's partitions follow its own length and
+    # the launch's partition count, which does not depend on the order of the
+    # batch, so reordering the sequences (their queries, table rows and
+    # lengths) reorders the output rows and changes no bit
+    lens = [9000, 0, 1, 300, 2048, 17, 4100, 640]
+    case = pi.make_case(8, lens, 32, 8, 128, 16, dtype="bf16", seed=37, holes=[(2, 0), (4, 5)])
+    perm = np.random.default_rng(41).permutation(case.batch)
+    shuffled = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    shuffled.q = case.q[perm]
+    shuffled.q_bits = case.q_bits[perm] if case.q_bits is not None else None
+    shuffled.block_tables = np.ascontiguousarray(case.block_tables[perm])
+    shuffled.context_lens = np.ascontiguousarray(case.context_lens[perm])
+    ref = oracle.decode_case(case)
+    for parts in (None, 0, 1, 6):
+        say(f"batch order, P={parts}")
+        a = run_gpu(case, gpu, num_partitions=parts)
+        b = run_gpu(shuffled, gpu, num_partitions=parts)
+        assert_close(to_f64(a), ref, "bf16", f"batch order P={parts}")
+        assert torch.equal(b, a[torch.from_numpy(perm).to(gpu)]), f"P={parts}: rows differ"
+
+
 def test_split_halves_equal_fused_call(gpu):
     case = pi.make_config_case(4)
     d = DeviceCase(case, gpu)
