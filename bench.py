@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--reps", type=int, default=REPS,
                     help="timed regions of --steps steps each (median reported)")
     ap.add_argument("--no-read-ceiling", action="store_true",
-                    help="skip the plain streaming-read leg")
+                    help="skip the plain streaming-read and gather legs")
     ap.add_argument("--timeline", action="store_true",
                     help="instead of the bench line, the per-workgroup timeline of the timed "
                          "workload's last graph-replayed step (libpa_decode_timeline.so)")
@@ -209,6 +209,9 @@ def probe_lib():
         lib.pa_probe_read.restype = ctypes.c_int
         lib.pa_probe_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         lib.pa_probe_stamp.restype = ctypes.c_int
+        V, I = ctypes.c_void_p, ctypes.c_int
+        lib.pa_probe_gather.argtypes = [V, V, V, V, I, I, I, I, I, I, V, V]
+        lib.pa_probe_gather.restype = ctypes.c_int
         _PROBE = lib
     return _PROBE
 
@@ -330,18 +333,31 @@ def measure(case, dev, steps, warmup, use_graph, num_partitions=0, reps=REPS):
 def sweep_read(dev, steps, warmup, use_graph):
     """The plain streaming read (libpa_read_probe.so) of the headline's bytes
     at other launch shapes: 256 / 512 / 1024 workgroups of 4 waves, 8 / 16 /
-    32 KB in flight per wave."""
+    32 KB in flight per wave; then the decode kernel's own gather of the
+    headline's K and V rows (pa_probe_gather) at the launch's partition count
+    and at twice it."""
     import pa_inputs as pi
     nbytes = pi.make_config_case(5).algorithmic_bytes()
     points = []
     for wgs in (256, 512, 1024):
         for depth in (8, 16, 32):
             med, best, nb = read_ceiling(dev, nbytes, wgs, steps, warmup, use_graph, depth=depth)
-            points.append(dict(workgroups=wgs, kb_in_flight_per_wave=depth, bytes=nb,
+            points.append(dict(kind="read", workgroups=wgs, kb_in_flight_per_wave=depth, bytes=nb,
                                us=round(med * 1e6, 3), us_min=round(best * 1e6, 3),
                                GBps=round(nb / med / 1e9, 1)))
             log(f"read {nb} bytes, {wgs} workgroups, {depth} KB per wave: {med * 1e6:.2f} us "
                 f"({nb / med / 1e9:.0f} GB/s)")
+    # the decode kernel's own gather of the headline's K and V rows (no
+    # arithmetic, no merge) at its partition count and at twice it
+    w = Workload(pi.make_config_case(5), dev, 0)
+    for P in (w.P, 2 * w.P):
+        med, best = gather_ceiling(w, steps, warmup, use_graph, partitions=P)
+        nb = w.case.algorithmic_bytes()
+        points.append(dict(kind="gather", partitions=P, workgroups=w.case.num_kv_heads * P,
+                           kb_in_flight_per_wave=16, bytes=nb, us=round(med * 1e6, 3),
+                           us_min=round(best * 1e6, 3), GBps=round(nb / med / 1e9, 1)))
+        log(f"gather of the headline's rows, {P} partitions: {med * 1e6:.2f} us")
+    del w
     return dict(metric="plain streaming read us of the headline's bytes by launch shape",
                 unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
                 data="synthetic", points=points)
@@ -370,6 +386,37 @@ def read_ceiling(dev, nbytes, workgroups, steps, warmup, use_graph, reps=REPS, d
     del bufs
     torch.cuda.empty_cache()
     return med, best, nbytes
+
+
+def gather_ceiling(w, steps, warmup, use_graph, reps=REPS, partitions=None):
+    """Seconds per launch (median, min) of pa_probe_gather over the
+    workload's rotation copies: the decode kernel's own gather of the K and V
+    rows -- its grid of (kv head, sequence, partition) workgroups at the
+    launch's partition count, the same tiles, table reads and loads -- with no
+    arithmetic and no merge.  None where the probe does not take the shape
+    (rows of 1 KB, more than 65535 sequences)."""
+    import torch
+    c = w.case
+    P = partitions or w.P
+    row = c.head_dim * (4 if c.dtype == "f32" else 2)
+    lib = probe_lib()
+    x0 = w.copies[0]
+    sink = torch.zeros(c.batch * c.num_kv_heads * P, dtype=torch.int32, device=x0["k"].device)
+    args = lambda x: (x["k"].data_ptr(), x["v"].data_ptr(), x["t"].data_ptr(), x["n"].data_ptr(),
+                      c.batch, c.num_kv_heads, row, c.block_size, c.max_blocks, P,
+                      sink.data_ptr())
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = lib.pa_probe_gather(*args(x0), stream)
+    if rc == -3:
+        return None
+    if rc != 0:
+        raise RuntimeError(f"pa_probe_gather failed: {rc}")
+
+    def fn(i, s):
+        if lib.pa_probe_gather(*args(w.copies[i % w.ncopies]), s) != 0:
+            raise RuntimeError("pa_probe_gather failed")
+
+    return summarize(time_region(fn, steps, warmup, use_graph, w.ncopies, reps)[0])
 
 
 def strip_c_comments(text):
@@ -903,6 +950,12 @@ def main():
     grid = c.num_kv_heads * c.batch * w.P * w.v_slices
     ncopies, P, v_slices, kname = w.ncopies, w.P, w.v_slices, w.kernel_name()
     t_events = w.event_median
+    gather = None
+    if not args.no_read_ceiling:
+        gather = gather_ceiling(w, args.steps, args.warmup, use_graph, args.reps)
+        if gather is not None:
+            log(f"gather ceiling: the kernel's own K/V gather ({P} partitions, no arithmetic) "
+                f"in {gather[0] * 1e6:.2f} us (min {gather[1] * 1e6:.2f})")
     del w
     torch.cuda.empty_cache()
 
@@ -947,6 +1000,12 @@ def main():
             "read_ceiling_GBps": round(read["bytes"] / read["us"] / 1e3, 1),
             "read_ceiling_bytes": read["bytes"],
             "frac_of_read_ceiling": round(read["us"] / (t_dom * 1e6), 4),
+        })
+    if gather is not None:
+        roofline.update({
+            "gather_ceiling_us": round(gather[0] * 1e6, 3),
+            "gather_ceiling_us_min": round(gather[1] * 1e6, 3),
+            "frac_of_gather_ceiling": round(gather[0] / t_dom, 4),
         })
     line = {
         "metric": METRIC,

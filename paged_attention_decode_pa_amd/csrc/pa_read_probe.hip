@@ -1,12 +1,13 @@
-// pa_read_probe.hip -- a plain streaming read, the measuring stick for the
-// decode kernel's bandwidth.  It reads a buffer once with the decode kernel's
-// load shape (workgroups of 4 waves, 16-byte non-temporal raw buffer loads,
-// 16 KB in flight per wave) and does nothing else: no table, no scores, no
-// merge.  Its time for the bytes one decode step reads is the time no kernel
-// with that load shape can beat on this part.  Beside it, a one-thread kernel
-// that writes the device clock, which the benchmark captures around its timed
+// pa_read_probe.hip -- measuring sticks for the decode kernel's bandwidth.  A
+// plain streaming read of a buffer with the decode kernel's load shape
+// (workgroups of 4 waves, 16-byte non-temporal raw buffer loads, 16 KB in
+// flight per wave), and the decode kernel's own gather of the K and V rows
+// through the block table: both do nothing else -- no scores, no softmax, no
+// merge -- so their times for the bytes of one decode step bound what the
+// kernel can reach with that shape.  Beside them, a one-thread kernel that
+// writes the device clock, which the benchmark captures around its timed
 // steps.  Built into its own library, libpa_read_probe.so; the decode library
-// does not contain or call either.
+// does not contain or call any of them.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -58,6 +59,98 @@ __global__ __launch_bounds__(kWaves * kWave) void read_kernel(const char *src, l
     }
 }
 
+// The decode kernel's gather without its arithmetic: grid (kv head, sequence,
+// partition) of 4 waves, the sequence's 16-token tiles dealt in runs of two to
+// the P * 4 (partition, wave) lanes in turn, two tiles in flight per wave, the
+// table entry of each tile read as a scalar, and per tile one buffer
+// descriptor over its live rows of this kv head for K and one for V (rows
+// past the context and -1 blocks read as zeros without a memory access).
+// Each load instruction of a wave covers whole rows (ROWB / 16 lanes per
+// row), 16 bytes per lane, non-temporal.  The words read are folded with xor,
+// and each workgroup writes the xor of all of them to sink, so the xor of the
+// whole sink is the xor of every live K and V row once, whatever the deal.
+template <int ROWB>
+__global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
+    const char *k, const char *v, const int *table, const int *lens, int max_blocks, int P,
+    int tok_bytes, long long blk_bytes, int tiles_log2, unsigned *sink) {
+    constexpr int kDepth = 2;                    // tiles in flight per wave
+    constexpr int kLoads = ROWB / 64;            // 16-byte loads per lane per 16-row tile
+    constexpr int kLanesPerRow = ROWB / 16;
+    const int kvh = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int *trow = table + (long long)b * max_blocks;
+    int ctx = lens[b];
+    const int cap = max_blocks << (tiles_log2 + 4);
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int ntiles = (ctx + 15) / 16;
+    const int first = kDepth * (part * kWaves + wave);
+    const int stride = P * kWaves * kDepth;
+    const char *kb = k + (long long)kvh * ROWB;
+    const char *vb = v + (long long)kvh * ROWB;
+    unsigned off[kLoads];
+#pragma unroll
+    for (int m = 0; m < kLoads; ++m) {
+        const int c = m * kWave + lane;
+        off[m] = (c / kLanesPerRow) * tok_bytes + 16 * (c % kLanesPerRow);
+    }
+    auto table_at = [&](int j) -> int {
+        const int e = j >> tiles_log2;
+        return trow[e < max_blocks ? e : max_blocks - 1];
+    };
+    u32x4 kr[kDepth][kLoads], vr[kDepth][kLoads];
+    auto issue = [&](int s, int j, int id) {
+        int nl = ctx - 16 * j;
+        nl = nl < 16 ? nl : 16;
+        if (j >= ntiles || id < 0) nl = 0;
+        const long long o = nl > 0 ? (long long)id * blk_bytes +
+                                         (long long)(j & ((1 << tiles_log2) - 1)) * 16 * tok_bytes
+                                   : 0;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb + o), 0, nl * tok_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb + o), 0, nl * tok_bytes, 0x00020000);
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m)
+            kr[s][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off[m], 0, 2));
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m)
+            vr[s][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off[m], 0, 2));
+    };
+    unsigned acc = 0;
+    auto fold = [&](int s) {
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m)
+            acc ^= kr[s][m][0] ^ kr[s][m][1] ^ kr[s][m][2] ^ kr[s][m][3] ^ vr[s][m][0] ^
+                   vr[s][m][1] ^ vr[s][m][2] ^ vr[s][m][3];
+    };
+    int nid[kDepth];
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) nid[s] = table_at(first + s);
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) issue(s, first + s, nid[s]);
+    for (int g = 1; first + stride * g < ntiles; ++g) {
+        const int nbase = first + stride * g;
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) nid[s] = table_at(nbase + s);
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) {
+            fold(s);
+            issue(s, nbase + s, nid[s]);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) fold(s);
+    __shared__ unsigned folded[kWaves * kWave];
+    folded[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned a = 0;
+        for (int i = 0; i < kWaves * kWave; ++i) a ^= folded[i];
+        sink[((long long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x] = a;
+    }
+}
+
 // One thread writes the device's constant-rate clock (s_memrealtime, 100 MHz)
 // to dst[0].
 __global__ void stamp_kernel(unsigned long long *dst) {
@@ -69,6 +162,35 @@ __global__ void stamp_kernel(unsigned long long *dst) {
 extern "C" int pa_probe_stamp(unsigned long long *dst, void *stream) {
     if (!dst) return -1;
     hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), dst);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+extern "C" int pa_probe_gather(const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, const int32_t *context_lens, int B,
+                               int Hkv, int row_bytes, int block_size, int max_blocks,
+                               int partitions, unsigned *sink, void *stream) {
+    if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return -1;
+    if (B < 0 || Hkv <= 0 || max_blocks <= 0 || partitions <= 0) return -2;
+    if ((row_bytes != 128 && row_bytes != 256 && row_bytes != 512) ||
+        block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0 ||
+        partitions > 4096 || B > 65535 || Hkv > 65535 ||
+        (long long)max_blocks * block_size > (1LL << 30) ||
+        16LL * Hkv * row_bytes > 0x7FFFFFFFLL)
+        return -3;
+    if (B == 0) return 0;
+    int tiles_log2 = 0;
+    while ((16 << tiles_log2) < block_size) ++tiles_log2;
+    const int tok = Hkv * row_bytes;
+    const long long blk = (long long)block_size * tok;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const char *k = static_cast<const char *>(k_cache);
+    const char *v = static_cast<const char *>(v_cache);
+    const dim3 grid(Hkv, B, partitions), block(kWaves * kWave);
+    switch (row_bytes) {
+        case 128: hipLaunchKernelGGL(gather_kernel<128>, grid, block, 0, s, k, v, block_tables, context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink); break;
+        case 256: hipLaunchKernelGGL(gather_kernel<256>, grid, block, 0, s, k, v, block_tables, context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink); break;
+        default: hipLaunchKernelGGL(gather_kernel<512>, grid, block, 0, s, k, v, block_tables, context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink); break;
+    }
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -351,7 +351,7 @@ def test_read_probe_library_exports_its_header():
     text = open(os.path.join(os.path.dirname(HEADER), "pa_read_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
-    assert names == ["pa_probe_read", "pa_probe_stamp"]
+    assert names == ["pa_probe_gather", "pa_probe_read", "pa_probe_stamp"]
     lib = ctypes.CDLL(hip_build.PROBE_LIB)
     fn = lib.pa_probe_read
     fn.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
@@ -363,6 +363,17 @@ def test_read_probe_library_exports_its_header():
     assert fn(16, 1024, 4, 12, 16, None) == -3
     lib.pa_probe_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     assert lib.pa_probe_stamp(None, None) == -1
+    g = lib.pa_probe_gather
+    V, I = ctypes.c_void_p, ctypes.c_int
+    g.argtypes = [V, V, V, V, I, I, I, I, I, I, V, V]
+    ok = dict(k=16, v=32, t=48, n=64, B=1, Hkv=8, row=256, bs=16, mb=1024, P=32, sink=80)
+    gcall = lambda **kw: g(*[dict(ok, **kw)[x] for x in ok], None)
+    assert gcall(k=None) == -1 and gcall(sink=None) == -1
+    assert gcall(B=-1) == -2 and gcall(Hkv=0) == -2 and gcall(mb=0) == -2 and gcall(P=0) == -2
+    assert gcall(row=1024) == -3 and gcall(row=96) == -3 and gcall(bs=8) == -3
+    assert gcall(bs=48) == -3 and gcall(P=4097) == -3 and gcall(B=65536) == -3
+    assert gcall(mb=1 << 27, bs=16) == -3              # more than 2^30 tokens per row
+    assert gcall(B=0) == 0                              # nothing to read: no launch
 
 
 

@@ -1,12 +1,18 @@
 """bench.py end to end on the GPU: one short run of a small workload prints
 one JSON line with the fields the benchmark contract names, consistent with
 each other."""
+import ctypes
 import json
 import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
+import torch
+
+import pa_inputs as pi
+from gpu_util import DeviceCase, say
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -46,6 +52,9 @@ def test_bench_prints_one_consistent_json_line(gpu):
     assert 0 < d["us_per_step"] <= 1.02 * d["us_per_step_events"]
     assert r["read_ceiling_us"] > 0 and r["read_ceiling_bytes"] >= bytes_per_step
     assert abs(r["frac_of_read_ceiling"] - r["read_ceiling_us"] / r["avg_launch_us"]) < 1e-3
+    # and the kernel's own gather, with no arithmetic and no merge
+    assert r["gather_ceiling_us"] > 0 and r["gather_ceiling_us_min"] <= r["gather_ceiling_us"]
+    assert abs(r["frac_of_gather_ceiling"] - r["gather_ceiling_us"] / r["avg_launch_us"]) < 1e-3
 
 
 def test_bench_case_option_reports_its_launch(gpu):
@@ -65,3 +74,51 @@ def test_bench_case_option_reports_its_launch(gpu):
     assert c["num_partitions"] == 3 and c["v_slices"] == 2
     assert d["per_config"] == [] and d["cpu_baseline"] is None
     assert d["roofline"]["traffic"] is None   # counters were taken on another workload
+
+
+def live_words_xor(case):
+    """The xor of every 32-bit word of every live K and V row (t < context
+    length, table entry >= 0) of every (sequence, kv head), on the host."""
+    k = case.k_cache if case.dtype == "f32" else case.k_bits
+    v = case.v_cache if case.dtype == "f32" else case.v_bits
+    kw = np.ascontiguousarray(k).view(np.uint32)
+    vw = np.ascontiguousarray(v).view(np.uint32)
+    acc = np.uint32(0)
+    for b in range(case.batch):
+        n = int(case.context_lens[b])
+        t = np.arange(n)
+        blk = case.block_tables[b, t // case.block_size]
+        keep = blk >= 0
+        rows = (blk[keep], (t % case.block_size)[keep])
+        for w in (kw, vw):
+            sel = w[rows[0], rows[1]]          # [live][Hkv][words]
+            if sel.size:
+                acc ^= np.bitwise_xor.reduce(sel.reshape(-1))
+    return int(acc)
+
+
+@pytest.mark.parametrize("dtype,d,bs", [("bf16", 128, 16), ("bf16", 64, 64), ("f16", 256, 16),
+                                        ("f32", 128, 32)])
+def test_gather_probe_reads_every_live_row_once(gpu, dtype, d, bs):
+    # the gather ceiling's probe reads what a decode step reads: the xor of
+    # its whole sink is the xor of every live K and V row, each once (a row
+    # read twice or skipped changes it), for any partition count
+    from paged_attention_decode_pa_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    V, I = ctypes.c_void_p, ctypes.c_int
+    lib.pa_probe_gather.argtypes = [V, V, V, V, I, I, I, I, I, I, V, V]
+    case = pi.make_case(5, [3000, 0, 1, 777, 64], 32, 8, d, bs, dtype=dtype, seed=43,
+                        holes=[(0, 2), (3, 1)], max_blocks=200)
+    dc = DeviceCase(case, gpu)
+    want = live_words_xor(case)
+    elem = 4 if dtype == "f32" else 2
+    for P in (1, 3, 32, 200):
+        say(f"gather probe {dtype} d={d} bs={bs} P={P}")
+        sink = torch.zeros(case.batch * case.num_kv_heads * P, dtype=torch.int32, device=gpu)
+        rc = lib.pa_probe_gather(dc.k.data_ptr(), dc.v.data_ptr(), dc.table.data_ptr(),
+                                 dc.lens.data_ptr(), case.batch, case.num_kv_heads, d * elem,
+                                 bs, case.max_blocks, P, sink.data_ptr(), None)
+        assert rc == 0
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert int(got) == want, f"P={P}: {int(got):#x} != {want:#x}"

@@ -55,3 +55,19 @@ def test_ablation_kernels_use_no_scratch():
                 assert len(n) == len(sc) and n, (variant, src)
                 bad = [a for a, b in zip(n, sc) if b != 0]
                 assert not bad, f"{variant}: kernels using scratch: {bad}"
+
+
+def test_probe_kernels_use_no_scratch():
+    """The measuring kernels of libpa_read_probe.so keep to registers too: a
+    spill would slow the ceilings they set."""
+    with tempfile.TemporaryDirectory() as tmp:
+        results = hip_build.compile_objects(hip_build.PROBE_SOURCES, tmp,
+                                            extra=["-Rpass-analysis=kernel-resource-usage"])
+    for src, _, rc, err in results:
+        assert rc == 0, err[-2000:]
+        n = re.findall(r"Function Name: (\S+)", err)
+        s = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", err)]
+        assert len(n) == len(s) and n, src
+        assert sum("gather_kernel" in x for x in n) == 3 and sum("read_kernel" in x for x in n) == 3
+        bad = [a for a, b in zip(n, s) if b != 0]
+        assert not bad, f"probe kernels using scratch: {bad}"
