@@ -75,7 +75,7 @@ def parse():
                     help="partition count for the timed workload (0 = the heuristic, "
                          "-1 = the heuristic told that all lengths are equal)")
     ap.add_argument("--variant", default=None,
-                    choices=["valu_qk", "no_vsplit", "ordered", "timeline"],
+                    choices=["valu_qk", "no_vsplit", "ordered", "timeline", "breakdown"],
                     help="time an ablation build instead of the library: valu_qk runs the "
                          "q.K product on the vector ALUs instead of the matrix cores; "
                          "no_vsplit never splits V's head dim over two workgroups; ordered "
@@ -90,6 +90,11 @@ def parse():
     ap.add_argument("--timeline", action="store_true",
                     help="instead of the bench line, the per-workgroup timeline of the timed "
                          "workload's last graph-replayed step (libpa_decode_timeline.so)")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="instead of the bench line, what a fused split adds to its own gather: "
+                         "the step, the step stopped after its partial sums and after its "
+                         "stream (libpa_decode_breakdown.so, timing only), and the gather "
+                         "probe, timed interleaved")
     ap.add_argument("--timeline-runs", type=int, default=1, metavar="N",
                     help="with --timeline: measure N times in one process (the XCD that runs "
                          "each kv head's units moves from one measurement to the next) and add "
@@ -445,12 +450,14 @@ def strip_c_comments(text):
 
 
 def kernel_source_sha256():
-    """One digest over the library's code: every file under csrc/ (sorted by
-    name, each name followed by its text) and the C header, with comments and
-    whitespace runs removed, so that edits to comments alone keep it."""
+    """One digest over the library's code: every file under csrc/ but the
+    probes' (sorted by name, each name followed by its text) and the C
+    header, with comments and whitespace runs removed, so that edits to
+    comments alone keep it."""
     import hashlib
     csrc = os.path.join(ROOT, "paged_attention_decode_pa_amd", "csrc")
-    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    # (the probes' source builds a library of its own, not this one)
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f != "pa_read_probe.hip"]
     files.append(os.path.join(ROOT, "include", "pa_decode.h"))
     h = hashlib.sha256()
     for f in files:
@@ -724,6 +731,54 @@ def pct(xs, q):
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
 
+def breakdown(case, dev, steps, warmup, use_graph, parts, rounds=3):
+    """What a fused split adds to its own gather.  The library's step (behind
+    the parity gate), the breakdown library (include/pa_breakdown.h) at stage
+    0 (the whole step), stopped after the partial sums (no ticket, no merge)
+    and after the stream (no epilogue), and pa_probe_gather (the same rows
+    gathered the same way, no arithmetic), timed interleaved over the same
+    rotation copies, `rounds` times each; medians in microseconds.  The
+    stopped launches write no output, so only the library is checked."""
+    import ctypes
+    import torch
+    import paged_attention_decode_pa_amd as pa
+    w, _, _, err = measure(case, dev, steps, warmup, use_graph, parts)
+    if w.P == 1:
+        raise SystemExit(f"{case.name}: a single pass (P = 1) has no split to break down")
+    main = w.lib
+    bd = pa.load_variant("breakdown")
+    bd.pa_breakdown_stop_after.argtypes = [ctypes.c_int]
+    keys = ("step", "step_breakdown_build", "stop_after_partials", "stop_after_stream",
+            "gather")
+    times = {k: [] for k in keys}
+    region = lambda: summarize(time_region(w.step, steps, warmup, use_graph, w.ncopies)[0])[0]
+    try:
+        for _ in range(rounds):
+            w.lib = main
+            times["step"].append(region())
+            w.lib = bd
+            for stage, key in ((0, "step_breakdown_build"), (1, "stop_after_partials"),
+                               (2, "stop_after_stream")):
+                if bd.pa_breakdown_stop_after(stage) != 0:
+                    raise RuntimeError("pa_breakdown_stop_after failed")
+                times[key].append(region())
+            bd.pa_breakdown_stop_after(0)
+            g = gather_ceiling(w, steps, warmup, use_graph)
+            times["gather"].append(g[0] if g else float("nan"))
+    finally:
+        bd.pa_breakdown_stop_after(0)
+    us = {k: round(float(np.median(v)) * 1e6, 3) for k, v in times.items()}
+    log("breakdown (us): " + ", ".join(f"{k} {v}" for k, v in us.items()))
+    out = dict(workload=case.name, partitions=w.P, v_slices=w.v_slices, rounds=rounds,
+               steps=steps, max_abs_err=err, us=us,
+               merge_us=round(us["step"] - us["stop_after_partials"], 3),
+               epilogue_us=round(us["stop_after_partials"] - us["stop_after_stream"], 3),
+               stream_over_gather=round(us["stop_after_stream"] / us["gather"], 4),
+               step_over_gather=round(us["step"] / us["gather"], 4))
+    del w
+    return out
+
+
 def timeline(case, dev, steps, warmup, use_graph, parts):
     """The per-workgroup stamps of the last step of the timed regions, from
     the timeline library (include/pa_timeline.h), summarised in microseconds
@@ -867,6 +922,8 @@ def child_legs(args, plan, python=None):
 def main():
     global VARIANT
     args = parse()
+    if args.timeline and args.breakdown:
+        sys.exit("--timeline and --breakdown are separate runs")
     VARIANT = "timeline" if args.timeline else args.variant
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -892,7 +949,8 @@ def main():
     # the per-config legs first, each in its own process, before this process
     # touches the GPU
     per_config = []
-    if not args.no_per_config and not args.case and not args.sweep:
+    if (not args.no_per_config and not args.case and not args.sweep and not args.timeline
+            and not args.breakdown):
         plan = [(c, 0) for c in (1, 2, 3, 4, 5) if c != args.workload] + [(4, 1), (5, 1)]
         per_config, crashed = child_legs(args, plan)
         if crashed:
@@ -924,6 +982,11 @@ def main():
                                 name=f"{dt} B={B} ctx={ctx} H={H} Hkv={Hkv} d={d} bs={bs}")
     else:
         headline = pi.make_config_case(args.workload)
+
+    if args.breakdown:
+        print(json.dumps(breakdown(headline, dev, min(args.steps, 1000), args.warmup, use_graph,
+                                   args.partitions)), flush=True)
+        return
 
     if args.timeline:
         runs = [timeline(headline, dev, min(args.steps, 200), args.warmup, use_graph,

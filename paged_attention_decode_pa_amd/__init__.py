@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 VARIANT_PATHS = {"valu_qk": os.path.join(HERE, "libpa_decode_valu_qk.so"),
                  "no_vsplit": os.path.join(HERE, "libpa_decode_no_vsplit.so"),
                  "ordered": os.path.join(HERE, "libpa_decode_ordered.so"),
-                 "timeline": os.path.join(HERE, "libpa_decode_timeline.so")}
+                 "timeline": os.path.join(HERE, "libpa_decode_timeline.so"),
+                 "breakdown": os.path.join(HERE, "libpa_decode_breakdown.so")}
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1

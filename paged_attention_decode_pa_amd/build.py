@@ -16,10 +16,13 @@ split; bench.py --variant no_vsplit).  A third, libpa_decode_ordered.so
 release / acquire in the memory model instead of by cache policy (bench.py
 --variant ordered); it computes the same bits.  libpa_decode_timeline.so
 (PA_TIMELINE=1) writes per-workgroup time stamps (include/pa_timeline.h;
-bench.py --timeline).  All else is identical.
+bench.py --timeline), and libpa_decode_breakdown.so (PA_BREAKDOWN=1) can stop
+a fused split after its partial sums or after its stream, for timing only
+(include/pa_breakdown.h; bench.py --breakdown).  All else is identical.
 
-libpa_read_probe.so (csrc/pa_read_probe.hip, include/pa_read_probe.h) is a
-plain streaming read with the decode kernel's load shape, the ceiling
+libpa_read_probe.so (csrc/pa_read_probe.hip, include/pa_read_probe.h) holds
+a plain streaming read with the decode kernel's load shape and the decode
+kernel's own gather of the K and V rows with no arithmetic, the ceilings
 bench.py measures the decode kernel against; nothing else loads it.
 """
 import os
@@ -45,6 +48,7 @@ VARIANTS = {
     "ordered": (os.path.join(HERE, "libpa_decode_ordered.so"), ["-DPA_ORDERED_TICKET=1"],
                 KERNEL_SOURCES),
     "timeline": (os.path.join(HERE, "libpa_decode_timeline.so"), ["-DPA_TIMELINE=1"], SOURCES),
+    "breakdown": (os.path.join(HERE, "libpa_decode_breakdown.so"), ["-DPA_BREAKDOWN=1"], SOURCES),
 }
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

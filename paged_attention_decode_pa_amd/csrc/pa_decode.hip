@@ -4,6 +4,7 @@
 // are in pa_kernels.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -13,6 +14,7 @@
 
 #include "pa_decode.h"
 #include "pa_internal.h"
+#include "pa_breakdown.h"
 #include "pa_timeline.h"
 
 namespace {
@@ -58,6 +60,12 @@ size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 // The timeline build's stamp buffer (pa_timeline_enable); null otherwise.
 unsigned long long *g_timeline = nullptr;
 unsigned g_timeline_cap = 0;
+
+#ifndef PA_BREAKDOWN
+#define PA_BREAKDOWN 0
+#endif
+// The breakdown build's stopping point (pa_breakdown_stop_after); 0 otherwise.
+std::atomic<int> g_stop_after{0};
 
 // Workspace layout: [B][H][P] float2 (max, sum) | [B][H][P][d] float partial
 // sums, the second region starting on a 256-byte boundary.
@@ -289,6 +297,7 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.merge_ways = 1;
     p.timeline = g_timeline;
     p.timeline_cap = g_timeline_cap;
+    p.stop_after = g_stop_after.load(std::memory_order_relaxed);
     p.max_tiles = table_tiles(max_blocks, block_size);
     p.qk_scale = scale * kLog2e;
     return p;
@@ -663,6 +672,14 @@ int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, 
     return run_merge(out, const_cast<void *>(workspace), B, H, P, d, dtype,
                      static_cast<hipStream_t>(stream));
 }
+
+#if PA_BREAKDOWN
+int pa_breakdown_stop_after(int stage) {
+    if (stage < 0 || stage > 2) return PA_ERR_VALUE;
+    g_stop_after.store(stage, std::memory_order_relaxed);
+    return PA_OK;
+}
+#endif
 
 #if PA_TIMELINE
 int pa_timeline_enable(int workgroups) {

@@ -78,13 +78,17 @@ struct Params {
     int max_tiles;        // max_blocks * block_size / 16
     int part_tiles_log2;  // a sequence of n tiles uses min(P, ceil(n / 2^this)) partitions,
     int solo_tiles;       // or one when n <= solo_tiles
-    int merge_ways;       // fused merge shared by the last 1, 2 or 4 arrivals (1 unless
-                          // every workgroup of the launch can be resident at once)
+    int merge_ways;       // fused merge shared by the last 1, 2, 4, 8 or 16 arrivals (1
+                          // unless every workgroup of the launch can be resident at once)
     float qk_scale;       // scale * log2(e)
     // Timeline build only (PA_TIMELINE=1): kTimelineSlots stamps per
     // workgroup for the first timeline_cap workgroups of a launch; else null.
     unsigned long long *timeline;
     unsigned timeline_cap;
+    // Breakdown build only (PA_BREAKDOWN=1): where a fused split stops, for
+    // timing -- 0 the whole step, 1 after the partial sums are stored (no
+    // ticket, no merge), 2 after the stream (no epilogue); 0 in the library.
+    int stop_after;
 };
 
 // Stamps per workgroup in the timeline build (pa_timeline.h gives the layout).

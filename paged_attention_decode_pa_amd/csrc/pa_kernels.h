@@ -577,6 +577,14 @@ __device__ __forceinline__ unsigned long long stamp_now() {
     return __builtin_amdgcn_s_memrealtime();
 }
 
+#ifndef PA_BREAKDOWN
+#define PA_BREAKDOWN 0
+#endif
+// Whether a fused split may stop early for timing (p.stop_after): 0 in the
+// library, 1 in the breakdown library libpa_decode_breakdown.so, whose early
+// stops write no output (include/pa_breakdown.h).
+constexpr bool kBreakdown = PA_BREAKDOWN != 0;
+
 #ifndef PA_ORDERED_TICKET
 #define PA_ORDERED_TICKET 0
 #endif
@@ -929,6 +937,19 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     }
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) update_slot(s);  // the last group
+    if constexpr (kBreakdown && kFusedMerge) {
+        if (p.stop_after == 2) {
+            // stop after the stream: the state is kept live (every load and
+            // update is needed for it) and nothing is written
+            float x = st.l + st.m;
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < VE; ++e) x += st.acc[h][e];
+            asm volatile("; stream state %0" ::"v"(x));
+            return;
+        }
+    }
     if constexpr (kTimeline) {
         if (tl && lane == 0 && wave < 4) tl[1 + wave] = stamp_now();
     }
@@ -1032,6 +1053,9 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     }
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
+        if constexpr (kBreakdown) {
+            if (p.stop_after == 1) return;  // the partial sums are stored; no ticket
+        }
         // Publish this partition and take a ticket.  The ticket of (b, kvh)
         // is 64 bits, an arrival count (low half) and a generation (high
         // half).  Of the n = VS * busy workgroups, the last to arrive (count

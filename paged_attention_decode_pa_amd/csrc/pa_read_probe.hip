@@ -80,11 +80,20 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int *trow = table + (long long)b * max_blocks;
+    auto table_at = [&](int j) -> int {
+        const int e = j >> tiles_log2;
+        return trow[e < max_blocks ? e : max_blocks - 1];
+    };
+    // the length and the first group's table entries leave together, as in
+    // the decode kernel (a lane's first tiles do not depend on the length)
+    const int first = kDepth * (part * kWaves + wave);
     int ctx = lens[b];
+    int nid[kDepth];
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) nid[s] = table_at(first + s);
     const int cap = max_blocks << (tiles_log2 + 4);
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     const int ntiles = (ctx + 15) / 16;
-    const int first = kDepth * (part * kWaves + wave);
     const int stride = P * kWaves * kDepth;
     const char *kb = k + (long long)kvh * ROWB;
     const char *vb = v + (long long)kvh * ROWB;
@@ -94,10 +103,6 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
         const int c = m * kWave + lane;
         off[m] = (c / kLanesPerRow) * tok_bytes + 16 * (c % kLanesPerRow);
     }
-    auto table_at = [&](int j) -> int {
-        const int e = j >> tiles_log2;
-        return trow[e < max_blocks ? e : max_blocks - 1];
-    };
     u32x4 kr[kDepth][kLoads], vr[kDepth][kLoads];
     auto issue = [&](int s, int j, int id) {
         int nl = ctx - 16 * j;
@@ -124,9 +129,6 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
             acc ^= kr[s][m][0] ^ kr[s][m][1] ^ kr[s][m][2] ^ kr[s][m][3] ^ vr[s][m][0] ^
                    vr[s][m][1] ^ vr[s][m][2] ^ vr[s][m][3];
     };
-    int nid[kDepth];
-#pragma unroll
-    for (int s = 0; s < kDepth; ++s) nid[s] = table_at(first + s);
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) issue(s, first + s, nid[s]);
     for (int g = 1; first + stride * g < ntiles; ++g) {
@@ -141,14 +143,15 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
     }
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) fold(s);
-    __shared__ unsigned folded[kWaves * kWave];
-    folded[threadIdx.x] = acc;
+    // an xor butterfly over the wave, then the 4 waves' words through LDS
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) acc ^= __shfl_xor(acc, o);
+    __shared__ unsigned folded[kWaves];
+    if (lane == 0) folded[wave] = acc;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned a = 0;
-        for (int i = 0; i < kWaves * kWave; ++i) a ^= folded[i];
-        sink[((long long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x] = a;
-    }
+    if (threadIdx.x == 0)
+        sink[((long long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x] =
+            folded[0] ^ folded[1] ^ folded[2] ^ folded[3];
 }
 
 // One thread writes the device's constant-rate clock (s_memrealtime, 100 MHz)

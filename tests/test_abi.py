@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pa.EXPORTS)
 
 
-@pytest.mark.parametrize("variant", ["valu_qk", "no_vsplit", "ordered", "timeline"])
+@pytest.mark.parametrize("variant", ["valu_qk", "no_vsplit", "ordered", "timeline", "breakdown"])
 def test_ablation_library_exports_the_same_functions(variant):
     lib = pa.load_variant(variant)
     for name in declared_functions():
@@ -443,3 +443,23 @@ def test_timeline_calls_only_in_the_timeline_library():
     assert tl.pa_timeline_enable(0) == pa.PA_ERR_VALUE
     assert tl.pa_timeline_copy(None, 4) == pa.PA_ERR_NULL
     assert tl.pa_timeline_copy(16, 4) == pa.PA_ERR_VALUE   # nothing enabled yet
+
+
+def test_breakdown_call_only_in_the_breakdown_library():
+    import ctypes
+    text = open(os.path.join(os.path.dirname(HEADER), "pa_breakdown.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+    assert names == ["pa_breakdown_stop_after"]
+    bd = pa.load_variant("breakdown")
+    assert hasattr(bd, names[0]) and not hasattr(pa.load(), names[0])
+    for other in ("timeline", "ordered"):
+        assert not hasattr(pa.load_variant(other), names[0])
+    bd.pa_breakdown_stop_after.argtypes = [ctypes.c_int]
+    try:
+        assert bd.pa_breakdown_stop_after(3) == pa.PA_ERR_VALUE
+        assert bd.pa_breakdown_stop_after(-1) == pa.PA_ERR_VALUE
+        for stage in (1, 2, 0):
+            assert bd.pa_breakdown_stop_after(stage) == pa.PA_OK
+    finally:
+        bd.pa_breakdown_stop_after(0)

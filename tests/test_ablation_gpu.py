@@ -15,6 +15,10 @@ split it removes.
 libpa_decode_timeline.so (per-workgroup time stamps): the library's exact
 bits, and stamps in causal order.
 
+libpa_decode_breakdown.so (a fused split stopped early, for timing): at stage
+0 the library's exact bits; its stopped launches write no output and leave
+the tickets as they were, so the next whole step is exact again.
+
 Their timings only mean something if they compute the same decode step."""
 import ctypes
 import math
@@ -150,3 +154,32 @@ def test_timeline_build(gpu):
         assert sorted(count[u].tolist()) == list(range(P * vs))  # one ticket each
         assert merger[u].sum() == ways[u][0]                     # the last `ways` arrivals
         assert role[u & (count == P * vs - 1)][0] == ways[u][0]  # the last one among them
+
+
+@pytest.mark.parametrize("cid", [2, 4, 5])
+def test_breakdown_build(gpu, cid):
+    # workload 2 is a fused split with V split, 4 and 5 fused splits; every
+    # partition of them publishes partial sums, so none writes out directly
+    bd = pa.load_variant("breakdown")
+    bd.pa_breakdown_stop_after.argtypes = [ctypes.c_int]
+    case = pi.make_config_case(cid)
+    c = case
+    d = DeviceCase(case, gpu)
+    ref = run_variant(case, gpu, 0, variant=None)
+    try:
+        for stage in (0, 1, 2, 0, 2, 1, 0):
+            assert bd.pa_breakdown_stop_after(stage) == 0
+            say(f"breakdown build, workload {cid}, stage {stage}")
+            out = torch.full_like(d.q, 7.0)
+            rc = bd.pa_decode(out.data_ptr(), d.q.data_ptr(), d.k.data_ptr(), d.v.data_ptr(),
+                              d.table.data_ptr(), d.lens.data_ptr(), c.batch, c.num_heads,
+                              c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks,
+                              float(c.scale), d.dtype, torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, pa.strerror(rc)
+            torch.cuda.synchronize()
+            if stage == 0:
+                assert torch.equal(out, ref), "stage 0 differs from the library"
+            else:
+                assert (out == 7.0).all(), f"stage {stage} wrote output"
+    finally:
+        bd.pa_breakdown_stop_after(0)

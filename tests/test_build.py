@@ -39,7 +39,7 @@ def test_ablation_kernels_use_no_scratch():
     import os
     with tempfile.TemporaryDirectory() as tmp:
         pending = []
-        for variant in ("valu_qk", "ordered", "timeline"):
+        for variant in ("valu_qk", "ordered", "timeline", "breakdown"):
             _, flags, _ = hip_build.VARIANTS[variant]
             srcs = [x for x in hip_build.KERNEL_SOURCES if variant != "valu_qk" or "f32" not in x]
             out = os.path.join(tmp, variant)
