@@ -340,7 +340,8 @@ def sweep_read(dev, steps, warmup, use_graph):
     at other launch shapes: 256 / 512 / 1024 workgroups of 4 waves, 8 / 16 /
     32 KB in flight per wave; then the decode kernel's own gather of the
     headline's K and V rows (pa_probe_gather) at the launch's partition count
-    and at twice it."""
+    and at twice it; and an empty launch (the one-thread clock kernel), the
+    floor under any step."""
     import pa_inputs as pi
     nbytes = pi.make_config_case(5).algorithmic_bytes()
     points = []
@@ -363,6 +364,20 @@ def sweep_read(dev, steps, warmup, use_graph):
                            us_min=round(best * 1e6, 3), GBps=round(nb / med / 1e9, 1)))
         log(f"gather of the headline's rows, {P} partitions: {med * 1e6:.2f} us")
     del w
+    # the floor under any step: a launch of a one-thread kernel that only
+    # writes the clock, replayed back to back like the decode steps
+    import torch
+    lib = probe_lib()
+    slot = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def empty(i, stream):
+        if lib.pa_probe_stamp(slot.data_ptr(), stream) != 0:
+            raise RuntimeError("pa_probe_stamp failed")
+
+    med, best = summarize(time_region(empty, steps, warmup, use_graph, 1)[0])
+    points.append(dict(kind="empty", workgroups=1, us=round(med * 1e6, 3),
+                       us_min=round(best * 1e6, 3)))
+    log(f"empty launch: {med * 1e6:.2f} us")
     return dict(metric="plain streaming read us of the headline's bytes by launch shape",
                 unit="us", higher_is_better=False, n_gpus=1, steps=steps, warmup=warmup,
                 data="synthetic", points=points)
