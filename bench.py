@@ -749,8 +749,9 @@ def pct(xs, q):
 def breakdown(case, dev, steps, warmup, use_graph, parts, rounds=3):
     """What a fused split adds to its own gather.  The library's step (behind
     the parity gate), the breakdown library (include/pa_breakdown.h) at stage
-    0 (the whole step), stopped after the partial sums (no ticket, no merge)
-    and after the stream (no epilogue), and pa_probe_gather (the same rows
+    0 (the whole step), stopped after the partial sums are stored (no ticket,
+    no merge), after the waves' sums are combined (nothing stored) and after
+    the stream (no epilogue), and pa_probe_gather (the same rows
     gathered the same way, no arithmetic), timed interleaved over the same
     rotation copies, `rounds` times each; medians in microseconds.  The
     stopped launches write no output, so only the library is checked."""
@@ -763,8 +764,8 @@ def breakdown(case, dev, steps, warmup, use_graph, parts, rounds=3):
     main = w.lib
     bd = pa.load_variant("breakdown")
     bd.pa_breakdown_stop_after.argtypes = [ctypes.c_int]
-    keys = ("step", "step_breakdown_build", "stop_after_partials", "stop_after_stream",
-            "gather")
+    keys = ("step", "step_breakdown_build", "stop_after_partials", "stop_after_combine",
+            "stop_after_stream", "gather")
     times = {k: [] for k in keys}
     region = lambda: summarize(time_region(w.step, steps, warmup, use_graph, w.ncopies)[0])[0]
     try:
@@ -772,8 +773,8 @@ def breakdown(case, dev, steps, warmup, use_graph, parts, rounds=3):
             w.lib = main
             times["step"].append(region())
             w.lib = bd
-            for stage, key in ((0, "step_breakdown_build"), (1, "stop_after_partials"),
-                               (2, "stop_after_stream")):
+            for stage, key in ((0, "step_breakdown_build"), (3, "stop_after_partials"),
+                               (2, "stop_after_combine"), (1, "stop_after_stream")):
                 if bd.pa_breakdown_stop_after(stage) != 0:
                     raise RuntimeError("pa_breakdown_stop_after failed")
                 times[key].append(region())
@@ -788,6 +789,8 @@ def breakdown(case, dev, steps, warmup, use_graph, parts, rounds=3):
                steps=steps, max_abs_err=err, us=us,
                merge_us=round(us["step"] - us["stop_after_partials"], 3),
                epilogue_us=round(us["stop_after_partials"] - us["stop_after_stream"], 3),
+               store_us=round(us["stop_after_partials"] - us["stop_after_combine"], 3),
+               combine_us=round(us["stop_after_combine"] - us["stop_after_stream"], 3),
                stream_over_gather=round(us["stop_after_stream"] / us["gather"], 4),
                step_over_gather=round(us["step"] / us["gather"], 4))
     del w

@@ -13,14 +13,14 @@
  * this library stops, in every workgroup that has tiles (a workgroup that
  * writes its sequence's output directly, as a single pass, is not stopped):
  *   0  nowhere: the whole step, as the library (the default);
- *   1  after storing the partition's partial sums (max, sum, weighted values):
- *      no ticket, no merge, so out is NOT written;
- *   2  after the stream of K and V rows and its arithmetic: no epilogue, no
- *      partial sums, no merge, so out is NOT written.
- * Stages 1 and 2 are for timing only.  They leave the tickets as they found
- * them, so stage 0 calls before and after them are correct.  The setting is
- * process-wide and read when a call is made.  Returns PA_OK or PA_ERR_VALUE
- * (stage outside 0..2).
+ *   1  after the stream of K and V rows and its arithmetic: no epilogue;
+ *   2  after the waves' sums are combined into the partition's partial sums
+ *      (max, sum, weighted values), which are not stored;
+ *   3  after storing the partial sums: no ticket, no merge.
+ * Stages 1 to 3 write no output and are for timing only.  They leave the
+ * tickets as they found them, so stage 0 calls before and after them are
+ * correct.  The setting is process-wide and read when a call is made.
+ * Returns PA_OK or PA_ERR_VALUE (stage outside 0..3).
  */
 #ifndef PA_BREAKDOWN_H
 #define PA_BREAKDOWN_H

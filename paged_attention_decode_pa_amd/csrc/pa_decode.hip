@@ -675,7 +675,7 @@ int pa_merge_partials(void *out, const void *workspace, size_t workspace_bytes, 
 
 #if PA_BREAKDOWN
 int pa_breakdown_stop_after(int stage) {
-    if (stage < 0 || stage > 2) return PA_ERR_VALUE;
+    if (stage < 0 || stage > 3) return PA_ERR_VALUE;
     g_stop_after.store(stage, std::memory_order_relaxed);
     return PA_OK;
 }

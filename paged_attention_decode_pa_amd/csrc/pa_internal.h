@@ -86,8 +86,9 @@ struct Params {
     unsigned long long *timeline;
     unsigned timeline_cap;
     // Breakdown build only (PA_BREAKDOWN=1): where a fused split stops, for
-    // timing -- 0 the whole step, 1 after the partial sums are stored (no
-    // ticket, no merge), 2 after the stream (no epilogue); 0 in the library.
+    // timing -- 0 the whole step, 1 after the stream (no epilogue), 2 after
+    // the waves' sums are combined (nothing stored), 3 after the partial sums
+    // are stored (no ticket, no merge); 0 in the library.
     int stop_after;
 };
 

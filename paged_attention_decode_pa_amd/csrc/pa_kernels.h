@@ -938,7 +938,7 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) update_slot(s);  // the last group
     if constexpr (kBreakdown && kFusedMerge) {
-        if (p.stop_after == 2) {
+        if (p.stop_after == 1) {
             // stop after the stream: the state is kept live (every load and
             // update is needed for it) and nothing is written
             float x = st.l + st.m;
@@ -1038,6 +1038,12 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
                 make_float2(o0, o1);
             if (e == 0 && vslice == 0) p.part_ml[bh * p.P + part] = make_float2(M, L);
         } else {
+            if constexpr (kBreakdown) {
+                if (p.stop_after == 2) {  // combined, kept live, not stored
+                    asm volatile("; combined %0 %1 %2 %3" ::"v"(o0), "v"(o1), "v"(M), "v"(L));
+                    continue;
+                }
+            }
             // (with V split, each slice stores its half; slice 0 the (max, sum))
             store_pair_coherent(p.part_acc + (bh * p.P + part) * D + vslice * DV + e, o0, o1);
             if (e == 0 && vslice == 0)
@@ -1054,7 +1060,8 @@ __global__ __launch_bounds__(NW * kWave) void pa_decode_kernel(Params p) {
     if constexpr (kFusedMerge) {
         if (direct || silent) return;
         if constexpr (kBreakdown) {
-            if (p.stop_after == 1) return;  // the partial sums are stored; no ticket
+            // stage 2: nothing stored; stage 3: the partial sums stored, no ticket
+            if (p.stop_after == 2 || p.stop_after == 3) return;
         }
         // Publish this partition and take a ticket.  The ticket of (b, kvh)
         // is 64 bits, an arrival count (low half) and a generation (high

@@ -457,9 +457,9 @@ def test_breakdown_call_only_in_the_breakdown_library():
         assert not hasattr(pa.load_variant(other), names[0])
     bd.pa_breakdown_stop_after.argtypes = [ctypes.c_int]
     try:
-        assert bd.pa_breakdown_stop_after(3) == pa.PA_ERR_VALUE
+        assert bd.pa_breakdown_stop_after(4) == pa.PA_ERR_VALUE
         assert bd.pa_breakdown_stop_after(-1) == pa.PA_ERR_VALUE
-        for stage in (1, 2, 0):
+        for stage in (1, 2, 3, 0):
             assert bd.pa_breakdown_stop_after(stage) == pa.PA_OK
     finally:
         bd.pa_breakdown_stop_after(0)

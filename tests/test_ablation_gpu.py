@@ -167,7 +167,7 @@ def test_breakdown_build(gpu, cid):
     d = DeviceCase(case, gpu)
     ref = run_variant(case, gpu, 0, variant=None)
     try:
-        for stage in (0, 1, 2, 0, 2, 1, 0):
+        for stage in (0, 1, 2, 3, 0, 3, 2, 1, 0):
             assert bd.pa_breakdown_stop_after(stage) == 0
             say(f"breakdown build, workload {cid}, stage {stage}")
             out = torch.full_like(d.q, 7.0)
