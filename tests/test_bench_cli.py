@@ -18,6 +18,37 @@ def test_more_than_one_gpu_is_refused():
     assert res.stdout == ""
 
 
+def test_timeline_and_breakdown_are_separate_runs():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--timeline",
+                          "--breakdown"], capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "separate runs" in res.stderr
+    assert res.stdout == ""
+
+
+def test_source_digest_leaves_out_the_probes(monkeypatch):
+    # the probes build a library of their own: a change to their source keeps
+    # the digest that ties counter summaries to the decode library's code,
+    # while a change to the library's own sources moves it
+    import builtins
+    base = bench.kernel_source_sha256()
+    real_open = builtins.open
+
+    def edited(name):
+        def fake_open(path, *a, **k):
+            f = real_open(path, *a, **k)
+            if os.path.basename(str(path)) != name:
+                return f
+            import io
+            return io.StringIO(f.read() + "\nint edited_for_the_test = 1;\n")
+        return fake_open
+
+    monkeypatch.setattr(builtins, "open", edited("pa_read_probe.hip"))
+    assert bench.kernel_source_sha256() == base
+    monkeypatch.setattr(builtins, "open", edited("pa_kernels.h"))
+    assert bench.kernel_source_sha256() != base
+
+
 def test_cpu_baseline_fields():
     import pa_inputs as pi
     case = pi.make_config_case(1)
