@@ -58,9 +58,12 @@
 // per wave), PA_K_ROWS (1 = the row K layout where k_rows_layout picks it,
 // 0 = the column layout everywhere), PA_KV_CACHE_POLICY (2 = non-temporal
 // K/V loads), PA_QK_VALU (0; 1 = the vector-ALU q.K of the ablation
-// library libpa_decode_valu_qk.so, which is built and tested) and
+// library libpa_decode_valu_qk.so, which is built and tested),
 // PA_ORDERED_TICKET (0; 1 = the fused merge ordered by release / acquire, the
-// ablation library libpa_decode_ordered.so, also built and tested).
+// ablation library libpa_decode_ordered.so, also built and tested), and two
+// measuring aids that change no arithmetic: PA_TIMELINE (per-workgroup time
+// stamps, libpa_decode_timeline.so) and PA_BREAKDOWN (a fused split stopped
+// after its stream, its combine or its stores, libpa_decode_breakdown.so).
 #ifndef PA_KERNELS_H
 #define PA_KERNELS_H
 
