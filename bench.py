@@ -215,7 +215,7 @@ def probe_lib():
         lib.pa_probe_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         lib.pa_probe_stamp.restype = ctypes.c_int
         V, I = ctypes.c_void_p, ctypes.c_int
-        lib.pa_probe_gather.argtypes = [V, V, V, V, I, I, I, I, I, I, V, V]
+        lib.pa_probe_gather.argtypes = [V, V, V, V, I, I, I, I, I, I, I, V, V]
         lib.pa_probe_gather.restype = ctypes.c_int
         _PROBE = lib
     return _PROBE
@@ -411,19 +411,21 @@ def read_ceiling(dev, nbytes, workgroups, steps, warmup, use_graph, reps=REPS, d
 def gather_ceiling(w, steps, warmup, use_graph, reps=REPS, partitions=None):
     """Seconds per launch (median, min) of pa_probe_gather over the
     workload's rotation copies: the decode kernel's own gather of the K and V
-    rows -- its grid of (kv head, sequence, partition) workgroups at the
-    launch's partition count, the same tiles, table reads and loads -- with no
-    arithmetic and no merge.  None where the probe does not take the shape
-    (rows of 1 KB, more than 65535 sequences)."""
+    rows -- its grid of (kv head, sequence, partition[, V slice]) workgroups
+    at the launch's partition count and V slices, the same tiles, table reads
+    and loads -- with no arithmetic and no merge.  None where the probe does
+    not take the shape (rows of 1 KB, more than 65535 sequences)."""
     import torch
     c = w.case
     P = partitions or w.P
     row = c.head_dim * (4 if c.dtype == "f32" else 2)
     lib = probe_lib()
     x0 = w.copies[0]
-    sink = torch.zeros(c.batch * c.num_kv_heads * P, dtype=torch.int32, device=x0["k"].device)
+    vs = w.v_slices
+    sink = torch.zeros(c.batch * c.num_kv_heads * P * vs, dtype=torch.int32,
+                       device=x0["k"].device)
     args = lambda x: (x["k"].data_ptr(), x["v"].data_ptr(), x["t"].data_ptr(), x["n"].data_ptr(),
-                      c.batch, c.num_kv_heads, row, c.block_size, c.max_blocks, P,
+                      c.batch, c.num_kv_heads, row, c.block_size, c.max_blocks, P, vs,
                       sink.data_ptr())
     stream = torch.cuda.current_stream().cuda_stream
     rc = lib.pa_probe_gather(*args(x0), stream)
@@ -881,7 +883,7 @@ def leg_row(cid, parts, dev, steps, warmup, use_graph, reps):
     import pa_inputs as pi
     w, ts, tmin, err = measure(pi.make_config_case(cid), dev, steps, warmup, use_graph, parts,
                                reps)
-    return dict(
+    row = dict(
         workload=cid, name=w.case.name, status="ok", partitions=w.P, v_slices=w.v_slices,
         path=("single-pass" if w.P == 1 else "split-KV + fused merge")
              + (", V split in two" if w.v_slices > 1 else ""),
@@ -890,6 +892,12 @@ def leg_row(cid, parts, dev, steps, warmup, use_graph, reps):
         pct_of_peak=round(100 * w.bytes / ts / 1e9 / HBM_PEAK_GBS, 1),
         launches_per_step=w.launches_per_step(), max_abs_err=err,
         rotation_copies=w.ncopies, algorithmic_bytes=w.bytes)
+    # the same rows gathered the same way (the launch's partitions and V
+    # slices) with no arithmetic
+    g = gather_ceiling(w, steps, warmup, use_graph, reps)
+    if g is not None:
+        row.update(gather_us=round(g[0] * 1e6, 3), frac_of_gather=round(g[0] / ts, 4))
+    return row
 
 
 # A child that ends on a signal or an abort has faulted or crashed: its

@@ -44,7 +44,10 @@ int pa_probe_read(const void *src, long long bytes, int workgroups, int depth, u
  * [pool][block_size][Hkv][row_bytes / element size] (device memory, 16-byte
  * aligned), block_tables [B][max_blocks] and context_lens [B] int32 (device
  * memory); row_bytes = d * element size, 128, 256 or 512.  The grid is
- * (Hkv, B, partitions) workgroups of 4 waves; a sequence's 16-token tiles are
+ * (Hkv, B, partitions * v_slices) workgroups of 4 waves; with v_slices = 2,
+ * as in the decode kernel's V-split launches, two workgroups serve each
+ * partition (z = 2 partition + slice), both reading all of K and each one
+ * half of every V row.  A sequence's 16-token tiles are
  * dealt in runs of two to the partitions * 4 (partition, wave) lanes in turn
  * (every partition takes part, whatever the length), each wave keeping two
  * tiles in flight, one scalar table read per tile, and one buffer descriptor
@@ -53,16 +56,18 @@ int pa_probe_read(const void *src, long long bytes, int workgroups, int depth, u
  * zeros without a memory access; every other entry used must be a valid pool
  * block.  Loads are 16 bytes per lane, non-temporal, each instruction
  * covering whole rows.  Workgroup (x, y, z) writes to sink[(z * B + y) * Hkv
- * + x] (device memory of B * Hkv * partitions words) the xor of every 32-bit
- * word it read, so the xor of the whole sink is that of every live K and V
- * row of every (sequence, kv head), each read once.  Enqueue only, on
- * `stream`.  Returns 0, -1 (NULL pointer), -2 (negative or zero size), -3
- * (row_bytes, block_size or partitions outside the supported set, B or Hkv
- * above 65535, or the size limits of pa_decode) or -7 (launch failed).
+ * + x] (device memory of B * Hkv * partitions * v_slices words) the xor of
+ * every 32-bit word it read, so the xor of the whole sink is that of every
+ * live K row of every (sequence, kv head) read v_slices times and every live
+ * V row read once.  Enqueue only, on `stream`.  Returns 0, -1 (NULL pointer),
+ * -2 (negative or zero size), -3 (row_bytes, block_size, partitions or
+ * v_slices outside the supported set, B or Hkv above 65535, or the size
+ * limits of pa_decode) or -7 (launch failed).
  */
 int pa_probe_gather(const void *k_cache, const void *v_cache, const int32_t *block_tables,
                     const int32_t *context_lens, int B, int Hkv, int row_bytes, int block_size,
-                    int max_blocks, int partitions, unsigned *sink, void *stream);
+                    int max_blocks, int partitions, int v_slices, unsigned *sink,
+                    void *stream);
 
 /*
  * pa_probe_stamp enqueues on `stream` a one-thread kernel that writes the

@@ -22,6 +22,17 @@ constexpr int kChunk = kWave * 16;  // bytes one load instruction of a wave cove
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// The xor of `acc` over the workgroup (valid in thread 0): a butterfly over
+// each wave, then the 4 waves' words through LDS.
+__device__ __forceinline__ unsigned fold_workgroup(unsigned acc, int wave, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) acc ^= __shfl_xor(acc, o);
+    __shared__ unsigned folded[kWaves];
+    if (lane == 0) folded[wave] = acc;
+    __syncthreads();
+    return folded[0] ^ folded[1] ^ folded[2] ^ folded[3];
+}
+
 // Workgroup g reads bytes [g * slice, min((g + 1) * slice, bytes)); wave w
 // takes runs of DEPTH consecutive 1 KB chunks, run r of the workgroup going
 // to wave r % kWaves, all DEPTH loads of a run in flight before any is used.
@@ -49,14 +60,8 @@ __global__ __launch_bounds__(kWaves * kWave) void read_kernel(const char *src, l
 #pragma unroll
         for (int j = 0; j < DEPTH; ++j) acc ^= x[j][0] ^ x[j][1] ^ x[j][2] ^ x[j][3];
     }
-    __shared__ unsigned folded[kWaves * kWave];
-    folded[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned a = 0;
-        for (int i = 0; i < kWaves * kWave; ++i) a ^= folded[i];
-        sink[blockIdx.x] = a;
-    }
+    const unsigned a = fold_workgroup(acc, wave, lane);
+    if (threadIdx.x == 0) sink[blockIdx.x] = a;
 }
 
 // The decode kernel's gather without its arithmetic: grid (kv head, sequence,
@@ -66,17 +71,24 @@ __global__ __launch_bounds__(kWaves * kWave) void read_kernel(const char *src, l
 // descriptor over its live rows of this kv head for K and one for V (rows
 // past the context and -1 blocks read as zeros without a memory access).
 // Each load instruction of a wave covers whole rows (ROWB / 16 lanes per
-// row), 16 bytes per lane, non-temporal.  The words read are folded with xor,
-// and each workgroup writes the xor of all of them to sink, so the xor of the
-// whole sink is the xor of every live K and V row once, whatever the deal.
-template <int ROWB>
+// row), 16 bytes per lane, non-temporal.  With VS = 2, as in the decode
+// kernel's V-split modes, two workgroups serve each partition (grid z = 2
+// partition + slice): both read all of K, each one half of every V row.  The
+// words read are folded with xor, and each workgroup writes the xor of all of
+// them to sink, so the xor of the whole sink is the xor of every live K row
+// read VS times and every live V row once, whatever the deal.
+template <int ROWB, int VS>
 __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
     const char *k, const char *v, const int *table, const int *lens, int max_blocks, int P,
     int tok_bytes, long long blk_bytes, int tiles_log2, unsigned *sink) {
     constexpr int kDepth = 2;                    // tiles in flight per wave
-    constexpr int kLoads = ROWB / 64;            // 16-byte loads per lane per 16-row tile
+    constexpr int kLoads = ROWB / 64;            // 16-byte K loads per lane per 16-row tile
     constexpr int kLanesPerRow = ROWB / 16;
-    const int kvh = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+    constexpr int kVLoads = kLoads / VS;         // the same for this slice of V
+    constexpr int kVLanesPerRow = kLanesPerRow / VS;
+    const int kvh = blockIdx.x, b = blockIdx.y;
+    const int part = VS > 1 ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
+    const int vslice = VS > 1 ? (int)(blockIdx.z & 1) : 0;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int *trow = table + (long long)b * max_blocks;
@@ -96,14 +108,19 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
     const int ntiles = (ctx + 15) / 16;
     const int stride = P * kWaves * kDepth;
     const char *kb = k + (long long)kvh * ROWB;
-    const char *vb = v + (long long)kvh * ROWB;
-    unsigned off[kLoads];
+    const char *vb = v + (long long)kvh * ROWB + vslice * (ROWB / VS);
+    unsigned off[kLoads], voff[kVLoads];
 #pragma unroll
     for (int m = 0; m < kLoads; ++m) {
         const int c = m * kWave + lane;
         off[m] = (c / kLanesPerRow) * tok_bytes + 16 * (c % kLanesPerRow);
     }
-    u32x4 kr[kDepth][kLoads], vr[kDepth][kLoads];
+#pragma unroll
+    for (int m = 0; m < kVLoads; ++m) {
+        const int c = m * kWave + lane;
+        voff[m] = (c / kVLanesPerRow) * tok_bytes + 16 * (c % kVLanesPerRow);
+    }
+    u32x4 kr[kDepth][kLoads], vr[kDepth][kVLoads];
     auto issue = [&](int s, int j, int id) {
         int nl = ctx - 16 * j;
         nl = nl < 16 ? nl : 16;
@@ -119,15 +136,15 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
         for (int m = 0; m < kLoads; ++m)
             kr[s][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off[m], 0, 2));
 #pragma unroll
-        for (int m = 0; m < kLoads; ++m)
-            vr[s][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off[m], 0, 2));
+        for (int m = 0; m < kVLoads; ++m)
+            vr[s][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[m], 0, 2));
     };
     unsigned acc = 0;
     auto fold = [&](int s) {
 #pragma unroll
-        for (int m = 0; m < kLoads; ++m)
-            acc ^= kr[s][m][0] ^ kr[s][m][1] ^ kr[s][m][2] ^ kr[s][m][3] ^ vr[s][m][0] ^
-                   vr[s][m][1] ^ vr[s][m][2] ^ vr[s][m][3];
+        for (int m = 0; m < kLoads; ++m) acc ^= kr[s][m][0] ^ kr[s][m][1] ^ kr[s][m][2] ^ kr[s][m][3];
+#pragma unroll
+        for (int m = 0; m < kVLoads; ++m) acc ^= vr[s][m][0] ^ vr[s][m][1] ^ vr[s][m][2] ^ vr[s][m][3];
     };
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) issue(s, first + s, nid[s]);
@@ -143,15 +160,9 @@ __global__ __launch_bounds__(kWaves * kWave) void gather_kernel(
     }
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) fold(s);
-    // an xor butterfly over the wave, then the 4 waves' words through LDS
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) acc ^= __shfl_xor(acc, o);
-    __shared__ unsigned folded[kWaves];
-    if (lane == 0) folded[wave] = acc;
-    __syncthreads();
+    const unsigned a = fold_workgroup(acc, wave, lane);
     if (threadIdx.x == 0)
-        sink[((long long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x] =
-            folded[0] ^ folded[1] ^ folded[2] ^ folded[3];
+        sink[((long long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x] = a;
 }
 
 // One thread writes the device's constant-rate clock (s_memrealtime, 100 MHz)
@@ -171,10 +182,10 @@ extern "C" int pa_probe_stamp(unsigned long long *dst, void *stream) {
 extern "C" int pa_probe_gather(const void *k_cache, const void *v_cache,
                                const int32_t *block_tables, const int32_t *context_lens, int B,
                                int Hkv, int row_bytes, int block_size, int max_blocks,
-                               int partitions, unsigned *sink, void *stream) {
+                               int partitions, int v_slices, unsigned *sink, void *stream) {
     if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return -1;
-    if (B < 0 || Hkv <= 0 || max_blocks <= 0 || partitions <= 0) return -2;
-    if ((row_bytes != 128 && row_bytes != 256 && row_bytes != 512) ||
+    if (B < 0 || Hkv <= 0 || max_blocks <= 0 || partitions <= 0 || v_slices <= 0) return -2;
+    if ((row_bytes != 128 && row_bytes != 256 && row_bytes != 512) || v_slices > 2 ||
         block_size < 16 || block_size > 256 || (block_size & (block_size - 1)) != 0 ||
         partitions > 4096 || B > 65535 || Hkv > 65535 ||
         (long long)max_blocks * block_size > (1LL << 30) ||
@@ -188,12 +199,24 @@ extern "C" int pa_probe_gather(const void *k_cache, const void *v_cache,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const char *k = static_cast<const char *>(k_cache);
     const char *v = static_cast<const char *>(v_cache);
-    const dim3 grid(Hkv, B, partitions), block(kWaves * kWave);
-    switch (row_bytes) {
-        case 128: hipLaunchKernelGGL(gather_kernel<128>, grid, block, 0, s, k, v, block_tables, context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink); break;
-        case 256: hipLaunchKernelGGL(gather_kernel<256>, grid, block, 0, s, k, v, block_tables, context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink); break;
-        default: hipLaunchKernelGGL(gather_kernel<512>, grid, block, 0, s, k, v, block_tables, context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink); break;
+    const dim3 grid(Hkv, B, partitions * v_slices), block(kWaves * kWave);
+#define PA_PROBE_GATHER(R, S)                                                                   \
+    hipLaunchKernelGGL((gather_kernel<R, S>), grid, block, 0, s, k, v, block_tables,            \
+                       context_lens, max_blocks, partitions, tok, blk, tiles_log2, sink)
+    if (v_slices == 1) {
+        switch (row_bytes) {
+            case 128: PA_PROBE_GATHER(128, 1); break;
+            case 256: PA_PROBE_GATHER(256, 1); break;
+            default: PA_PROBE_GATHER(512, 1); break;
+        }
+    } else {
+        switch (row_bytes) {
+            case 128: PA_PROBE_GATHER(128, 2); break;
+            case 256: PA_PROBE_GATHER(256, 2); break;
+            default: PA_PROBE_GATHER(512, 2); break;
+        }
     }
+#undef PA_PROBE_GATHER
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -365,13 +365,14 @@ def test_read_probe_library_exports_its_header():
     assert lib.pa_probe_stamp(None, None) == -1
     g = lib.pa_probe_gather
     V, I = ctypes.c_void_p, ctypes.c_int
-    g.argtypes = [V, V, V, V, I, I, I, I, I, I, V, V]
-    ok = dict(k=16, v=32, t=48, n=64, B=1, Hkv=8, row=256, bs=16, mb=1024, P=32, sink=80)
+    g.argtypes = [V, V, V, V, I, I, I, I, I, I, I, V, V]
+    ok = dict(k=16, v=32, t=48, n=64, B=1, Hkv=8, row=256, bs=16, mb=1024, P=32, vs=1, sink=80)
     gcall = lambda **kw: g(*[dict(ok, **kw)[x] for x in ok], None)
     assert gcall(k=None) == -1 and gcall(sink=None) == -1
     assert gcall(B=-1) == -2 and gcall(Hkv=0) == -2 and gcall(mb=0) == -2 and gcall(P=0) == -2
     assert gcall(row=1024) == -3 and gcall(row=96) == -3 and gcall(bs=8) == -3
     assert gcall(bs=48) == -3 and gcall(P=4097) == -3 and gcall(B=65536) == -3
+    assert gcall(vs=0) == -2 and gcall(vs=3) == -3
     assert gcall(mb=1 << 27, bs=16) == -3              # more than 2^30 tokens per row
     assert gcall(B=0) == 0                              # nothing to read: no launch
 

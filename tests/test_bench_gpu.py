@@ -76,9 +76,10 @@ def test_bench_case_option_reports_its_launch(gpu):
     assert d["roofline"]["traffic"] is None   # counters were taken on another workload
 
 
-def live_words_xor(case):
-    """The xor of every 32-bit word of every live K and V row (t < context
-    length, table entry >= 0) of every (sequence, kv head), on the host."""
+def live_words_xor(case, with_k=True):
+    """The xor of every 32-bit word of every live K (if with_k) and V row
+    (t < context length, table entry >= 0) of every (sequence, kv head), on
+    the host."""
     k = case.k_cache if case.dtype == "f32" else case.k_bits
     v = case.v_cache if case.dtype == "f32" else case.v_bits
     kw = np.ascontiguousarray(k).view(np.uint32)
@@ -90,7 +91,7 @@ def live_words_xor(case):
         blk = case.block_tables[b, t // case.block_size]
         keep = blk >= 0
         rows = (blk[keep], (t % case.block_size)[keep])
-        for w in (kw, vw):
+        for w in ((kw, vw) if with_k else (vw,)):
             sel = w[rows[0], rows[1]]          # [live][Hkv][words]
             if sel.size:
                 acc ^= np.bitwise_xor.reduce(sel.reshape(-1))
@@ -99,25 +100,29 @@ def live_words_xor(case):
 
 @pytest.mark.parametrize("dtype,d,bs", [("bf16", 128, 16), ("bf16", 64, 64), ("f16", 256, 16),
                                         ("f32", 128, 32)])
-def test_gather_probe_reads_every_live_row_once(gpu, dtype, d, bs):
+@pytest.mark.parametrize("vs", [1, 2])
+def test_gather_probe_reads_every_live_row_once(gpu, dtype, d, bs, vs):
     # the gather ceiling's probe reads what a decode step reads: the xor of
     # its whole sink is the xor of every live K and V row, each once (a row
-    # read twice or skipped changes it), for any partition count
+    # read twice or skipped changes it), for any partition count; with V
+    # split in two, every K row is read twice (and cancels) and each half of
+    # every V row once
     from paged_attention_decode_pa_amd import build as hip_build
     lib = ctypes.CDLL(hip_build.PROBE_LIB)
     V, I = ctypes.c_void_p, ctypes.c_int
-    lib.pa_probe_gather.argtypes = [V, V, V, V, I, I, I, I, I, I, V, V]
+    lib.pa_probe_gather.argtypes = [V, V, V, V, I, I, I, I, I, I, I, V, V]
     case = pi.make_case(5, [3000, 0, 1, 777, 64], 32, 8, d, bs, dtype=dtype, seed=43,
                         holes=[(0, 2), (3, 1)], max_blocks=200)
     dc = DeviceCase(case, gpu)
-    want = live_words_xor(case)
+    want = live_words_xor(case, with_k=vs == 1)
     elem = 4 if dtype == "f32" else 2
     for P in (1, 3, 32, 200):
-        say(f"gather probe {dtype} d={d} bs={bs} P={P}")
-        sink = torch.zeros(case.batch * case.num_kv_heads * P, dtype=torch.int32, device=gpu)
+        say(f"gather probe {dtype} d={d} bs={bs} P={P} V slices {vs}")
+        sink = torch.zeros(case.batch * case.num_kv_heads * P * vs, dtype=torch.int32,
+                           device=gpu)
         rc = lib.pa_probe_gather(dc.k.data_ptr(), dc.v.data_ptr(), dc.table.data_ptr(),
                                  dc.lens.data_ptr(), case.batch, case.num_kv_heads, d * elem,
-                                 bs, case.max_blocks, P, sink.data_ptr(), None)
+                                 bs, case.max_blocks, P, vs, sink.data_ptr(), None)
         assert rc == 0
         torch.cuda.synchronize()
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))

@@ -68,6 +68,6 @@ def test_probe_kernels_use_no_scratch():
         n = re.findall(r"Function Name: (\S+)", err)
         s = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", err)]
         assert len(n) == len(s) and n, src
-        assert sum("gather_kernel" in x for x in n) == 3 and sum("read_kernel" in x for x in n) == 3
+        assert sum("gather_kernel" in x for x in n) == 6 and sum("read_kernel" in x for x in n) == 3
         bad = [a for a, b in zip(n, s) if b != 0]
         assert not bad, f"probe kernels using scratch: {bad}"
