@@ -137,6 +137,19 @@ enum {
  * with at most one non-empty partition is written directly by partition 0
  * (zeros for an empty sequence); empty partitions do nothing.
  *
+ * Sharing the device.  The arrivals that share a merge wait on the GPU for
+ * the rest of their (sequence, kv head) to arrive, holding their workgroup
+ * slot meanwhile.  The library shares merges only when the launch's
+ * workgroups fit the device at once, and it keeps each launch's waiters
+ * below half of the workgroups the device holds at once (sharing among fewer
+ * arrivals where needed), so one such launch, or two running concurrently on
+ * different streams, always leave a slot for the workgroups they wait for.
+ * Kernels of other streams or processes only delay the wait, since they end.
+ * Three or more fused launches running at once could in principle fill every
+ * slot with waiters: a waiter gives up after 2^22 polls of its ticket
+ * (seconds) and writes NaN over its slice of the output rather than a wrong
+ * value.
+ *
  * Library-owned buffers.  The partials buffer and the ticket buffer are
  * allocated on first need per (device, stream) and grown when larger ones are
  * needed; growing synchronises `stream` once.  Tickets are zeroed on `stream`

@@ -295,6 +295,7 @@ Params make_params(const void *q, const void *k_cache, const void *v_cache,
     p.part_tiles_log2 = 0;  // every partition up to min(n, P) busy
     p.solo_tiles = 0;
     p.merge_ways = 1;
+    p.cus = 0;
     p.timeline = g_timeline;
     p.timeline_cap = g_timeline_cap;
     p.stop_after = g_stop_after.load(std::memory_order_relaxed);
@@ -565,6 +566,7 @@ int pa_decode_ex(void *out, const void *q, const void *k_cache, const void *v_ca
     attach_workspace(p, ws, d);
     p.counters = tickets;
     p.merge_ways = merge_ways(plan.mode, B, Hkv, v.G, d, P, cus);
+    p.cus = cus;
     return run_main(p, dtype, d, v.G, plan.mode, s);
 }
 
@@ -625,6 +627,7 @@ int pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void 
     p.counters = reinterpret_cast<int *>(base);
     attach_workspace(p, base + kScratchPartials, d);
     p.merge_ways = merge_ways(plan.mode, B, Hkv, v.G, d, P, cus);
+    p.cus = cus;
     return run_main(p, dtype, d, v.G, plan.mode, s);
 }
 

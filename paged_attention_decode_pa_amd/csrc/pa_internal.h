@@ -80,6 +80,7 @@ struct Params {
     int solo_tiles;       // or one when n <= solo_tiles
     int merge_ways;       // fused merge shared by the last 1, 2, 4, 8 or 16 arrivals (1
                           // unless every workgroup of the launch can be resident at once)
+    int cus;              // compute units of the device (the launcher's bound on waiters)
     float qk_scale;       // scale * log2(e)
     // Timeline build only (PA_TIMELINE=1): kTimelineSlots stamps per
     // workgroup for the first timeline_cap workgroups of a launch; else null.

@@ -1180,9 +1180,31 @@ __global__ __launch_bounds__(kWave) void pa_merge_kernel(MergeParams mp) {
 template <int DT, int D, int G, int MODE>
 hipError_t launch_instance(const Params &p, int nseq, hipStream_t stream) {
     if constexpr (mode_built(DT, D, G, MODE)) {
+        Params q = p;
+        if (q.merge_ways > 1) {
+            // The arrivals that wait to share a merge hold their compute unit
+            // while they wait.  Keep each launch's waiters (at most K - 1 per
+            // (sequence, kv head) unit) below half of the workgroups the
+            // device holds at once, so that even two such launches running
+            // together leave a slot for a workgroup they wait for.
+            static const int resident = [] {
+                int n = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n,
+                        reinterpret_cast<const void *>(
+                            &pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
+                        kWavesPerGroup * kWave, 0) != hipSuccess)
+                    n = 0;
+                return n;
+            }();
+            const long long units = (long long)nseq * q.Hkv;
+            while (q.merge_ways > 1 &&
+                   2 * units * (q.merge_ways - 1) >= (long long)q.cus * resident)
+                q.merge_ways /= 2;
+        }
         hipLaunchKernelGGL((pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
-                           dim3(p.Hkv, nseq, v_slices(MODE) * p.P),
-                           dim3(kWavesPerGroup * kWave), 0, stream, p);
+                           dim3(q.Hkv, nseq, v_slices(MODE) * q.P),
+                           dim3(kWavesPerGroup * kWave), 0, stream, q);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;

@@ -353,6 +353,44 @@ def test_pool_beyond_4_gib(gpu, dtype):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("shape", [(2, 2040, 128, 8, 128), (1, 16384, 32, 8, 128)],
+                         ids=["units16_G16", "headline"])
+def test_fused_launches_on_two_streams_at_once(gpu, shape):
+    # Two fused splits with shared merges enqueued on two streams without a
+    # sync between them, ten times over: each stream has buffers of its own,
+    # and the launcher keeps each launch's waiting arrivals below half of the
+    # device's workgroup slots, so the two always make progress together.
+    # The first shape (16 units of 16 query heads, one workgroup per compute
+    # unit, 16 partitions of 128 KiB of partials) would otherwise have every
+    # arrival wait.  Every output must match the oracle and repeat bitwise.
+    B, ctx, H, Hkv, d = shape
+    cases = [pi.make_case(B, ctx, H, Hkv, d, 16, dtype="bf16", seed=51 + i) for i in range(2)]
+    cus = pa.pa_device_num_cus(0)
+    for c in cases:
+        P, vs = pa.pa_plan(B, Hkv, d, c.max_blocks, 16, cus, H=H)
+        assert P > 1 and B * Hkv * P * vs <= cus and P * (H // Hkv) * d * 4 >= 48 << 10
+    refs = [oracle.decode_case(c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    devs = [DeviceCase(c, gpu) for c in cases]
+    for s, d_ in zip(streams, devs):   # a first call per stream sizes its buffers
+        with torch.cuda.stream(s):
+            pa.pa_decode(torch.empty_like(d_.q), *d_.args(), s)
+    torch.cuda.synchronize()
+    outs = [[], []]
+    say(f"two streams at once, B={B} ctx={ctx} H={H} Hkv={Hkv}")
+    for _ in range(10):
+        for i, (s, d_) in enumerate(zip(streams, devs)):
+            with torch.cuda.stream(s):
+                out = torch.empty_like(d_.q)
+                pa.pa_decode(out, *d_.args(), s)
+                outs[i].append(out)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert_close(to_f64(outs[i][0]), refs[i], "bf16", f"stream {i}")
+        for o in outs[i][1:]:
+            assert torch.equal(o, outs[i][0]), f"stream {i}: bits changed between calls"
+
+
 def test_non_default_stream(gpu):
     case = pi.make_config_case(3)
     s = torch.cuda.Stream()
