@@ -69,6 +69,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <utility>
@@ -1187,16 +1188,23 @@ hipError_t launch_instance(const Params &p, int nseq, hipStream_t stream) {
             // (sequence, kv head) unit) below half of the workgroups the
             // device holds at once, so that even two such launches running
             // together leave a slot for a workgroup they wait for.
-            static const int resident = [] {
+            // (queried once per instance; a failed query is not kept, and
+            // that call merges with the last arrival alone)
+            static std::atomic<int> cached{-1};
+            int resident = cached.load(std::memory_order_relaxed);
+            if (resident < 0) {
                 int n = 0;
                 if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                         &n,
                         reinterpret_cast<const void *>(
                             &pa_decode_kernel<DT, D, G, kWavesPerGroup, kDepth, MODE>),
-                        kWavesPerGroup * kWave, 0) != hipSuccess)
-                    n = 0;
-                return n;
-            }();
+                        kWavesPerGroup * kWave, 0) == hipSuccess) {
+                    cached.store(n, std::memory_order_relaxed);
+                    resident = n;
+                } else {
+                    resident = 0;
+                }
+            }
             const long long units = (long long)nseq * q.Hkv;
             while (q.merge_ways > 1 &&
                    2 * units * (q.merge_ways - 1) >= (long long)q.cus * resident)

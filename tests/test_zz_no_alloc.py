@@ -125,3 +125,46 @@ def test_noalloc_replayed_from_a_captured_graph(gpu, B, lens):
         pa.pa_decode_noalloc(oo, *od.args(), None)   # the array in between
         torch.cuda.synchronize()
     assert_close(to_f64(out), oracle.decode_case(case), "bf16", f"noalloc graph B={B}")
+
+
+FIRST_CALL_UNDER_CAPTURE = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + '/tests')
+import pa_inputs as pi, paged_attention_decode_pa_amd as pa
+from gpu_util import DeviceCase
+case = pi.make_case(1, 16384, 32, 8, 128, 16, dtype='bf16', seed=707)
+d = DeviceCase(case, torch.device('cuda:0'))
+out = torch.empty_like(d.q)
+s = torch.cuda.Stream()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.stream(s):
+    g.capture_begin()
+    pa.pa_decode_noalloc(out, *d.args(), s)   # the process's first decode call
+    g.capture_end()
+torch.cuda.synchronize()
+ref = torch.empty_like(d.q)
+pa.pa_decode(ref, *d.args(), None)
+torch.cuda.synchronize()
+for i in range(3):
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), f'replay {i}'
+print('ok', flush=True)
+"""
+
+
+def test_first_call_of_a_process_under_capture(gpu):
+    # a caller whose very first decode call is inside a graph capture: the
+    # launcher's one-time setup (the device array's address, its ticket
+    # clear, the kernel's occupancy for the shared merge) happens during the
+    # capture, and every replay still equals pa_decode bit for bit
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("noalloc: first call of a fresh process under graph capture")
+    res = subprocess.run([sys.executable, "-c", FIRST_CALL_UNDER_CAPTURE, root],
+                         capture_output=True, text=True, timeout=110)
+    assert res.returncode == 0, res.stderr[-2000:]
+    assert res.stdout.strip().endswith("ok")
