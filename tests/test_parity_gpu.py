@@ -391,6 +391,46 @@ def test_fused_launches_on_two_streams_at_once(gpu, shape):
             assert torch.equal(o, outs[i][0]), f"stream {i}: bits changed between calls"
 
 
+def test_serving_scale_batch(gpu):
+    # 128 sequences of 16K-32K tokens (3.1 M tokens, 12.8 GB of K and V rows
+    # per step), their blocks drawn with repetition from a pool of 8192
+    # (sequences sharing blocks, as with shared prefixes): the covering-batch
+    # launch (late query, long sequences split into 64-tile partitions) at
+    # the heuristic count and as a single pass; the oracle on sampled rows
+    # (the first, the longest, the shortest and three more)
+    B, H, Hkv, d, bs, W = 128, 32, 8, 128, 16, 2048
+    base = pi.make_case(1, 8192 * bs, H, Hkv, d, bs, dtype="bf16", seed=61, pool=8192)
+    qs = pi.make_case(B, 16, H, Hkv, d, bs, dtype="bf16", seed=62)
+    rng = np.random.default_rng(63)
+    lens = rng.integers(16384, W * bs + 1, size=B).astype(np.int32)
+    lens[0] = W * bs
+    table = rng.integers(0, 8192, size=(B, W)).astype(np.int32)
+    case = pi.Case(dtype="bf16", q=qs.q, k_cache=base.k_cache, v_cache=base.v_cache,
+                   block_tables=table, context_lens=lens, scale=base.scale, num_heads=H,
+                   num_kv_heads=Hkv, head_dim=d, block_size=bs, q_bits=qs.q_bits,
+                   k_bits=base.k_bits, v_bits=base.v_bits, seed=63, name="serving scale")
+    check_host_preconditions(case)
+    picks = sorted({0, int(lens.argmax()), int(lens.argmin()),
+                    *rng.choice(B, size=3, replace=False).tolist()})
+    sub = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    sub.q, sub.q_bits = case.q[picks], case.q_bits[picks]
+    sub.block_tables = np.ascontiguousarray(table[picks])
+    sub.context_lens = np.ascontiguousarray(lens[picks])
+    ref = oracle.decode_case(sub)
+    d_ = DeviceCase(case, gpu)
+    for parts in (None, 1):
+        say(f"serving scale: B={B}, {int(lens.sum())} tokens, P={parts}")
+        out = torch.empty_like(d_.q)
+        if parts is None:
+            pa.pa_decode(out, *d_.args(), None)
+        else:
+            pa.pa_decode_ex(out, *d_.args(), None, parts, 8192, None, 0)
+        torch.cuda.synchronize()
+        assert_close(to_f64(out[torch.tensor(picks, device=gpu)]), ref, "bf16",
+                     f"serving scale P={parts}")
+        assert torch.isfinite(out).all()
+
+
 def test_non_default_stream(gpu):
     case = pi.make_config_case(3)
     s = torch.cuda.Stream()
