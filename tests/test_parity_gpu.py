@@ -738,6 +738,47 @@ def test_graph_replay_matches_eager(gpu):
         assert torch.equal(other, eager)
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 16384, 32, 8, 128, "bf16"),     # 8-way shared merge
+    (4, 2048, 32, 8, 128, "bf16"),      # the last arrival alone
+    (2, 2040, 128, 8, 128, "bf16"),     # 16 query heads, ways bounded by the slots
+    (1, 12000, 4, 4, 256, "f16"),       # d = 256, V split
+], ids=["shared8", "lone", "G16", "d256"])
+def test_fused_merge_repeats_over_many_back_to_back_calls(gpu, shape):
+    # 50 fused calls back to back in one graph, each writing an output of its
+    # own, replayed 20 times: every one of the 1,000 outputs equals the eager
+    # result bit for bit, so no merge ever reads a partial sum before it is
+    # published or one left by the call before
+    B, ctx, H, Hkv, d, dtype = shape
+    case = pi.make_case(B, ctx, H, Hkv, d, 16, dtype=dtype, seed=ctx + H)
+    dc = DeviceCase(case, gpu)
+    ref = torch.empty_like(dc.q)
+    pa.pa_decode(ref, *dc.args(), None)
+    torch.cuda.synchronize()
+    assert_close(to_f64(ref), oracle.decode_case(case), dtype, "eager")
+    N, R = 50, 20
+    outs = torch.empty((N,) + tuple(dc.q.shape), dtype=dc.q.dtype, device=gpu)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pa.pa_decode(outs[0], *dc.args(), s)   # sizes this stream's buffers
+    torch.cuda.synchronize()
+    say(f"{N} fused calls in one graph, {R} replays: B={B} ctx={ctx} H={H} Hkv={Hkv} d={d}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        for i in range(N):
+            pa.pa_decode(outs[i], *dc.args(), s)
+        g.capture_end()
+    torch.cuda.synchronize()
+    for r in range(R):
+        outs.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = (outs.view(N, -1) == ref.view(1, -1)).all(dim=1)
+        assert bool(same.all()), f"replay {r}: calls {(~same).nonzero().flatten().tolist()} differ"
+
+
 def test_first_fused_call_on_a_fresh_stream(gpu):
     # the first call on a new (non-blocking) stream allocates and zeroes the
     # tickets; the zeroing is ordered before the fused kernel on that stream
